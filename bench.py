@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the online-softmax hot path on one MI355X.
+
+One step runs every stage of the path once, each on its own synthetic batch
+already resident in HBM:
+  softmax_f32   row_softmax, 65536 x 8192 fp32 logits N(0,1) x 30, block 8
+  softmax_bf16  row_softmax, 65536 x 8192 bf16 logits N(0,1) x 30, block 8
+  attn_nc       attn_fwd, B4 H16 S2048 D64 bf16, non-causal, scale 1/8
+  attn_causal   attn_fwd, B2 H32 S8192 D128 bf16, causal, scale 1/sqrt(128)
+  decode        attn_decode_splitkv, B16 H32 Lmax 32768 D128 bf16, 64 splits
+The headline value is the fp32 row softmax's HBM throughput (algorithmic
+bytes: one read and one write of every logit); every stage is reported with
+its own roofline fraction.  Each stage is timed with HIP events recorded on
+the stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "row-softmax HBM GB/s; attention fwd bf16 TFLOP/s (% of roofline), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "row_softmax": ["tiled_exact_attention_amd/csrc/softmax.hip", "tiled_exact_attention_amd/csrc/common.hpp"],
+    "attn_fwd": ["tiled_exact_attention_amd/csrc/attn_fwd.hip", "tiled_exact_attention_amd/csrc/common.hpp"],
+    "decode": ["tiled_exact_attention_amd/csrc/decode.hip", "tiled_exact_attention_amd/csrc/merge.hip",
+               "tiled_exact_attention_amd/csrc/common.hpp"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when none exist or the kernel's source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_hash") != source_hash(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows, heads and KV chunks shard with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tiled_exact_attention_amd as tea
+    from tiled_exact_attention_amd import inputs
+
+    tea.load_library()  # fail loudly before any work if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stages = args.stages.split(",")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    S = {}  # stage -> dict(fn, units, kind)
+    t0 = time.perf_counter()
+    if "softmax_f32" in stages or "softmax_bf16" in stages:
+        w = inputs.WORKLOADS["softmax_large"]
+        R, C = w["rows"], w["cols"]
+        for dt in ("f32", "bf16"):
+            name = f"softmax_{dt}"
+            if name not in stages:
+                continue
+            x = inputs.logits(R, C, 30.0, 202 if dt == "f32" else 205, dt).to(dev)
+            y = torch.empty_like(x)
+            es = 4 if dt == "f32" else 2
+            S[name] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 2 * es,
+                           kind="hbm", kernel="row_softmax",
+                           workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
+            log(f"inputs {name} ready ({time.perf_counter() - t0:.1f}s)")
+    if "attn_nc" in stages:
+        w = inputs.WORKLOADS["attn_noncausal"]
+        B, H, Sq, D = w["B"], w["H"], w["S"], w["D"]
+        q, k, v = (t.to(dev) for t in inputs.qkv(B, H, Sq, Sq, D, seed=301))
+        o = torch.empty_like(q)
+        S["attn_nc"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, causal=False, out=o)),
+                            units=4 * B * H * Sq * Sq * D, kind="mfma", kernel="attn_fwd",
+                            workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 non-causal")
+        log(f"inputs attn_nc ready ({time.perf_counter() - t0:.1f}s)")
+    if "attn_causal" in stages:
+        w = inputs.WORKLOADS["attn_causal"]
+        B, H, Sq, D = w["B"], w["H"], w["S"], w["D"]
+        q, k, v = (t.to(dev) for t in inputs.qkv(B, H, Sq, Sq, D, seed=401))
+        o = torch.empty_like(q)
+        S["attn_causal"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, causal=True, out=o)),
+                                units=4 * B * H * D * Sq * (Sq + 1) // 2, kind="mfma", kernel="attn_fwd",
+                                workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 causal")
+        log(f"inputs attn_causal ready ({time.perf_counter() - t0:.1f}s)")
+    if "decode" in stages:
+        w = inputs.WORKLOADS["decode_splitkv"]
+        B, H, Lmax, D, ns = w["B"], w["H"], w["Lmax"], w["D"], w["num_splits"]
+        q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=501)
+        qd, Kd, Vd, kvd = q.to(dev), K.to(dev), V.to(dev), kv.to(dev)
+        del K, V
+        ws = torch.empty(tea.attn_decode_workspace_bytes(B, H, D, ns), dtype=torch.uint8, device=dev)
+        od = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        tot = int(kv.sum())
+        S["decode"] = dict(fn=(lambda: tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=ns, workspace=ws,
+                                                               out=od)),
+                           units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode",
+                           workload=f"decode B{B} H{H} Lmax{Lmax} D{D} bf16 splits{ns} sum(kv_len)={tot}")
+        log(f"inputs decode ready ({time.perf_counter() - t0:.1f}s)")
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB write done")
+        del a, b
+
+    stream = torch.cuda.current_stream(dev)
+    names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode") if n in S]
+
+    def step(events=None):
+        for n in names:
+            if events is not None:
+                events[n][0].record(stream)
+            S[n]["fn"]()
+            if events is not None:
+                events[n][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    log(f"timed {args.steps} steps in {w1 - w0:.3f}s")
+    ms_per_step = (w1 - w0) * 1e3 / max(args.steps, 1)
+
+    paths = {}
+    for n in names:
+        t = [evs[i][n][0].elapsed_time(evs[i][n][1]) for i in range(args.steps)]
+        avg = float(np.mean(t))
+        s = S[n]
+        if s["kind"] == "hbm":
+            ach = s["units"] / (avg * 1e-3) / 1e9
+            peak, unit = HBM_PEAK_GBS, "GB/s"
+        else:
+            ach = s["units"] / (avg * 1e-3) / 1e12
+            peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+        paths[n] = {
+            "workload": s["workload"], "avg_ms": round(avg, 5), "min_ms": round(float(np.min(t)), 5),
+            "median_ms": round(float(np.median(t)), 5),
+            "roofline": {"bound": s["kind"], "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4), "traffic": measured_traffic(s["kernel"], n),
+                         "algorithmic_units_per_launch": s["units"]},
+        }
+
+    head = "softmax_f32" if "softmax_f32" in paths else names[0]
+    hp = paths[head]
+    out = {
+        "metric": METRIC,
+        "value": hp["roofline"]["achieved"],
+        "unit": hp["roofline"]["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": hp["workload"], "stages": names},
+        "roofline": hp["roofline"],
+        "paths": paths,
+    }
+    if "attn_causal" in paths:
+        out["attention_tflops"] = paths["attn_causal"]["roofline"]["achieved"]
+
+    if not args.no_cpu_baseline and "softmax_f32" in S:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(budget_s: float):
+    """The fp64 CPU oracle timed on a bounded sample of the headline
+    workload (the first rows of the same 65536 x 8192 fp32 batch), scaled to
+    the metric's unit (GB/s of logits read and written)."""
+    import oracle
+    from tiled_exact_attention_amd import inputs
+
+    C = inputs.WORKLOADS["softmax_large"]["cols"]
+    x = inputs.logits(65536, C, 30.0, 202, "f32").numpy()
+    rows = 256
+    t = 0.0
+    while True:
+        s = time.perf_counter()
+        oracle.softmax_rows(x[:rows])
+        t = time.perf_counter() - s
+        if t >= budget_s / 4 or rows >= 65536:
+            break
+        rows = min(65536, int(rows * max(2.0, budget_s / 4 / max(t, 1e-3))))
+    bytes_ = rows * C * 8
+    threads = oracle.num_threads()
+    return {"value": round(bytes_ / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of 65536 rows x {C} fp32 logits (same seeded batch), fp64 two-pass "
+                      f"oracle with OpenMP, {t:.2f}s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -63,6 +63,7 @@ def _load():
             lib.oracle_combine.argtypes = [D, D, P, D, D, P, I64, P, P, P]
             lib.oracle_merge_direct.argtypes = [P, P, P, I64, I64, I64, P, P, P]
             lib.oracle_abi_version.restype = ctypes.c_int
+            lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -270,3 +271,8 @@ def merge_direct(m, l, O):
 
 def abi_version() -> int:
     return int(_load().oracle_abi_version())
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(_load().oracle_num_threads())

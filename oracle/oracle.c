@@ -19,6 +19,7 @@
  *   - exported maxima and log-sum-exp values are in natural-log units.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -360,3 +361,15 @@ void oracle_merge_direct(const double* m, const double* l, const double* O, int6
 }
 
 int oracle_abi_version(void) { return 1; }
+
+/* Threads the oracle's OpenMP loops use. */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}

@@ -50,6 +50,7 @@ void oracle_merge_direct(const double* m, const double* l, const double* O, int6
                          double* m_out, double* l_out, double* O_out);
 
 int oracle_abi_version(void);
+int oracle_num_threads(void);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: libtea.so loads, exports every entry point
+include/tea.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_exact_attention_amd as tea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tea.h")
+
+NULL = None
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: validation fails first
+ODD = ctypes.c_void_p(0x10002)   # misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tea.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared()
+    for n in ("row_softmax", "attn_fwd", "attn_decode_splitkv", "merge_partials"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    for name in tea.EXPORTS:
+        assert name in _declared()
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tea_abi_version() == 1
+    for s in (tea.TEA_OK, tea.TEA_EINVAL, tea.TEA_EUNSUPPORTED, tea.TEA_EHIP):
+        assert lib.tea_status_string(s)
+    assert lib.tea_status_string(99) == b"unknown status"
+
+
+def test_row_softmax_validation(lib):
+    f = lib.row_softmax
+    assert f(NULL, NULL, 4, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EINVAL      # null x, y
+    assert f(FAKE, FAKE, -1, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EINVAL      # negative rows
+    assert f(FAKE, FAKE, 4, -8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EINVAL      # negative cols
+    assert f(FAKE, FAKE, 4, 8, 7, 8, NULL, NULL, NULL) == tea.TEA_EINVAL                 # bad dtype
+    assert f(FAKE, FAKE, 4, 8, tea.TEA_F32, -2, NULL, NULL, NULL) == tea.TEA_EINVAL      # bad block
+    assert f(FAKE, FAKE, 4, 8, tea.TEA_F32, 3, NULL, NULL, NULL) == tea.TEA_EUNSUPPORTED  # non power of two
+    assert f(FAKE, FAKE, 4, 16385, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EUNSUPPORTED
+    assert f(ODD, FAKE, 4, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EINVAL        # misaligned f32
+    y_overlap = ctypes.c_void_p(0x10000 + 16)
+    assert f(FAKE, y_overlap, 4, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_EINVAL  # partial overlap
+    assert f(NULL, NULL, 0, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_OK           # no rows: no-op
+
+
+def test_attn_fwd_validation(lib):
+    f = lib.attn_fwd
+    A = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)]
+    ok = dict(B=1, H=1, Sq=8, Sk=8, D=64, scale=0.125, causal=0, od=tea.TEA_BF16)
+
+    def call(ptrs=A, **kw):
+        a = {**ok, **kw}
+        return f(*ptrs, a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["scale"], a["causal"], a["od"], NULL, NULL)
+
+    assert call(D=96) == tea.TEA_EUNSUPPORTED
+    assert call(D=0) == tea.TEA_EINVAL
+    assert call(causal=1, Sk=9) == tea.TEA_EUNSUPPORTED
+    assert call(causal=2) == tea.TEA_EINVAL
+    assert call(scale=0.0) == tea.TEA_EINVAL
+    assert call(scale=float("nan")) == tea.TEA_EINVAL
+    assert call(scale=-1.0) == tea.TEA_EINVAL
+    assert call(od=5) == tea.TEA_EINVAL
+    assert call(B=-1) == tea.TEA_EINVAL
+    assert call(ptrs=[NULL, *A[1:]]) == tea.TEA_EINVAL
+    assert call(ptrs=[ODD, *A[1:]]) == tea.TEA_EINVAL
+    assert call(ptrs=[A[0], A[1], A[2], A[0]]) == tea.TEA_EINVAL  # o overlaps q
+    assert call(B=0) == tea.TEA_OK
+
+
+def test_decode_validation(lib):
+    f = lib.attn_decode_splitkv
+    assert lib.attn_decode_workspace_bytes(16, 32, 128, 64) >= 16 * 32 * 64 * (128 + 2) * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 128, 0) == 0
+    need = lib.attn_decode_workspace_bytes(2, 2, 128, 64)
+    P = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+         ctypes.c_void_p(0x50000)]
+    W = ctypes.c_void_p(0x100000)
+
+    def call(B=2, H=2, Lmax=100, D=128, S=64, scale=0.1, od=tea.TEA_BF16, ws=W, wsb=need, ptrs=P):
+        return f(*ptrs, B, H, Lmax, D, S, scale, od, ws, wsb, NULL)
+
+    assert call(S=0) == tea.TEA_EINVAL
+    assert call(S=1025) == tea.TEA_EINVAL
+    assert call(D=80) == tea.TEA_EUNSUPPORTED
+    assert call(wsb=need - 1) == tea.TEA_EINVAL
+    assert call(ws=NULL) == tea.TEA_EINVAL
+    assert call(Lmax=0) == tea.TEA_EINVAL
+    assert call(scale=0.0) == tea.TEA_EINVAL
+    assert call(ptrs=[P[0], P[1], P[2], NULL, P[4]]) == tea.TEA_EINVAL
+    assert call(B=0) == tea.TEA_OK
+
+
+def test_merge_validation(lib):
+    f = lib.merge_partials
+    m, l, O, o = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x90000))
+    assert f(m, l, O, 4, 0, 8, NULL, NULL, o, tea.TEA_F32, 1, NULL) == tea.TEA_EINVAL   # S = 0
+    assert f(m, l, O, 4, 8, 0, NULL, NULL, o, tea.TEA_F32, 1, NULL) == tea.TEA_EINVAL   # D = 0
+    assert f(m, l, O, -1, 8, 8, NULL, NULL, o, tea.TEA_F32, 1, NULL) == tea.TEA_EINVAL  # N < 0
+    assert f(m, l, O, 4, 8, 8, NULL, NULL, o, tea.TEA_BF16, 0, NULL) == tea.TEA_EINVAL  # unnormalised bf16
+    assert f(m, l, O, 4, 8, 8, NULL, NULL, o, tea.TEA_F32, 2, NULL) == tea.TEA_EINVAL
+    assert f(NULL, l, O, 4, 8, 8, NULL, NULL, o, tea.TEA_F32, 1, NULL) == tea.TEA_EINVAL
+    assert f(m, l, O, 4, 8, 8, NULL, NULL, O, tea.TEA_F32, 1, NULL) == tea.TEA_EINVAL   # output overlaps input
+    assert f(m, l, O, 0, 8, 8, NULL, NULL, o, tea.TEA_F32, 1, NULL) == tea.TEA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tea, "_lib", None)
+    monkeypatch.setattr(tea, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        tea.load_library()
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "tiled_exact_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src and "liboracle" not in src, fn
+                assert "oracle.h" not in src, fn

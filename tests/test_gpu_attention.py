@@ -1,0 +1,137 @@
+"""GPU parity of attn_fwd against the fp64 oracle (attention from its
+definition).
+
+Workloads: non-causal B4 H16 S2048 D64 and causal B2 H32 S8192 D128, bf16
+N(0,1), scale 1/sqrt(D), at full size on sampled query rows; small shapes in
+full, spanning several tiles with ragged tails; closed forms that hold
+exactly (one key, causal row 0) or in general (constant V); fp32 output,
+log-sum-exp, determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_amd as tea
+from tiled_exact_attention_amd import inputs
+from gpu_util import check_attention, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np32(t):
+    return t.float().numpy()
+
+
+def _run(q, k, v, causal, out_dtype=torch.bfloat16, scale=None):
+    D = q.shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    o, lse = tea.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal, out_dtype=out_dtype,
+                          return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse, scale
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 2, 17, 64, 127, 128, 129, 300])
+def test_small_full_parity(D, causal, S):
+    say(f"attn_fwd small S={S} D={D} causal={causal}")
+    q, k, v = inputs.qkv(2, 3, S, S, D, seed=S * 7 + D)
+    o, lse, scale = _run(q, k, v, causal)
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal)
+    check_attention(to_np(o), O, f"S={S} D={D} causal={causal}")
+    assert np.max(np.abs(to_np(lse) - L)) <= 1e-3
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 1000), (100, 1), (129, 65), (64, 1000), (333, 2049)])
+def test_noncausal_rectangular(Sq, Sk):
+    say(f"attn_fwd Sq={Sq} Sk={Sk}")
+    q, k, v = inputs.qkv(1, 4, Sq, Sk, 128, seed=Sq + Sk)
+    o, lse, scale = _run(q, k, v, False)
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, False)
+    check_attention(to_np(o), O, f"Sq={Sq} Sk={Sk}")
+    assert np.max(np.abs(to_np(lse) - L)) <= 1e-3
+
+
+def test_fp32_output():
+    """With an fp32 output the error left is P's rounding to bf16 before the
+    P V product (2^-9 relative per weight), so at most 2^-9 * max|v| per
+    entry; every entry is checked against that bound."""
+    say("attn_fwd fp32 output")
+    q, k, v = inputs.qkv(1, 2, 500, 500, 128, seed=3)
+    o, _, scale = _run(q, k, v, True, out_dtype=torch.float32)
+    O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), scale, True)
+    err = np.abs(to_np(o) - O)
+    bound = 2.0 ** -9 * np.abs(_np32(v)).max() + 1e-5
+    assert np.max(err) <= bound, f"fp32-output max abs err {np.max(err):.2e} > {bound:.2e}"
+    print(f"fp32-output max abs err {np.max(err):.2e} (bound {bound:.2e})")
+
+
+def test_closed_forms():
+    say("attn_fwd closed forms")
+    q, k, v = inputs.qkv(2, 2, 200, 200, 64, seed=4)
+    # one key: O = v0 exactly
+    o, lse, _ = _run(q, k[:, :, :1].contiguous(), v[:, :, :1].contiguous(), False)
+    assert torch.equal(o.cpu(), v[:, :, :1].expand(-1, -1, 200, -1))
+    # causal row 0 sees key 0 only
+    o, _, _ = _run(q, k, v, True)
+    assert torch.equal(o.cpu()[:, :, 0], v[:, :, 0])
+    # constant V: constant O (bf16 1.5 is exact)
+    vc = torch.full_like(v, 1.5)
+    o, _, _ = _run(q, k, vc, True, out_dtype=torch.float32)
+    assert float((o - 1.5).abs().max()) <= 1e-5
+    # large scale: logits far apart, no overflow or NaN
+    o, lse, _ = _run(q, k, v, False, scale=30.0)
+    O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), 30.0, False)
+    check_attention(to_np(o), O, "scale 30")
+
+
+def test_empty_keys_give_zero():
+    say("attn_fwd Sk=0")
+    q = torch.randn(1, 2, 10, 64, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=DEV)
+    o, lse = tea.attn_fwd(q, k, k, causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(lse == -math.inf)
+
+
+def test_deterministic():
+    say("attn_fwd determinism")
+    q, k, v = (t.to(DEV) for t in inputs.qkv(2, 4, 1000, 1000, 128, seed=5))
+    a = tea.attn_fwd(q, k, v, causal=True)
+    b = tea.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def _sample_rows(B, H, S, n, seed, causal):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in list(range(0, 4)) + [63, 64, 127, 128, 129, S - 129, S - 128, S - 1] + list(rng.integers(0, S, n)):
+        b, h = int(rng.integers(0, B)), int(rng.integers(0, H))
+        rows.append((b * H + h) * S + int(i))
+    if causal:
+        rows += [(b * H + h) * S + i for b in range(B) for h in (0, H - 1) for i in (0, 1, 255)]
+    return np.unique(np.array(rows, np.int64))
+
+
+@pytest.mark.parametrize("cfg", ["attn_noncausal", "attn_causal"])
+def test_full_size_sampled(cfg):
+    w = inputs.WORKLOADS[cfg]
+    B, H, S, D, causal = w["B"], w["H"], w["S"], w["D"], w["causal"]
+    seed = 301 if cfg == "attn_noncausal" else 401
+    say(f"attn_fwd full size {cfg} B{B} H{H} S{S} D{D} causal={causal}")
+    q, k, v = inputs.qkv(B, H, S, S, D, seed=seed)
+    o, lse, scale = _run(q, k, v, causal)
+    assert bool(torch.isfinite(o).all())
+    rows = _sample_rows(B, H, S, 160, seed, causal)
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal, rows=rows)
+    got = o.reshape(-1, D).cpu()[torch.from_numpy(rows)]
+    err = check_attention(to_np(got), O, cfg)
+    assert np.max(np.abs(to_np(lse).reshape(-1)[rows] - L)) <= 1e-3
+    print(f"{cfg}: max abs err {err:.3e} over {len(rows)} sampled rows")

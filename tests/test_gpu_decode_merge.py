@@ -1,0 +1,155 @@
+"""GPU parity of attn_decode_splitkv and merge_partials against the fp64
+oracle.
+
+Decode: B16 H32, one query, KV length uniform in [1, 32768], D128, 64 splits
+at full size on sampled (b, h) pairs and by properties at any size; lengths
+at chunk and tile edges (including L < 64, where chunks are empty, and
+L = 0); other split counts.  Merge: random partials against the merged state
+written out directly; the empty state as identity; all-empty rows; any S and
+D; agreement of different tree shapes up to rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_amd as tea
+from tiled_exact_attention_amd import inputs
+from gpu_util import check_attention, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _decode_ref(q, K, V, kv, scale, pairs):
+    O, lse = oracle.decode(q[:, :, 0], K, V, kv, scale, pairs=pairs, widen=lambda t: t.float().numpy())
+    return O
+
+
+@pytest.mark.parametrize("lengths", [[1, 2, 63, 64], [65, 511, 512, 513], [1000, 4096, 32767, 32768], [0, 5, 0, 70]])
+@pytest.mark.parametrize("splits", [1, 2, 64, 1024])
+def test_decode_edge_lengths(lengths, splits):
+    say(f"decode lengths={lengths} splits={splits}")
+    B, H, D = len(lengths), 3, 128
+    Lmax = max(max(lengths), 1)
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=sum(lengths) + splits, kv_len=np.array(lengths))
+    scale = 1.0 / math.sqrt(D)
+    o = tea.attn_decode_splitkv(q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV), num_splits=splits, scale=scale)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    ref = _decode_ref(q, K, V, kv.numpy(), scale, pairs)
+    check_attention(to_np(o).reshape(-1, D), ref, f"lengths={lengths} splits={splits}")
+    for n, (b, h) in enumerate(pairs):
+        if lengths[b] == 0:
+            assert torch.all(o[b, h] == 0)
+
+
+def test_decode_d64_and_fp32_out():
+    say("decode D=64 fp32 out")
+    B, H, D, Lmax = 3, 4, 64, 3000
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=9, kv_len=np.array([3000, 17, 1234]))
+    o = tea.attn_decode_splitkv(q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV), num_splits=64, scale=0.125,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    ref = _decode_ref(q, K, V, kv.numpy(), 0.125, pairs)
+    check_attention(to_np(o).reshape(-1, D), ref, "D64 fp32", atol=2e-3)
+
+
+def test_decode_full_size_sampled():
+    w = inputs.WORKLOADS["decode_splitkv"]
+    B, H, Lmax, D, S = w["B"], w["H"], w["Lmax"], w["D"], w["num_splits"]
+    say(f"decode full size B{B} H{H} Lmax{Lmax} D{D} splits{S}")
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=501)
+    scale = 1.0 / math.sqrt(D)
+    qd, Kd, Vd, kvd = q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV)
+    o = tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=S, scale=scale)
+    o2 = tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=S, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)  # deterministic: no atomics
+    assert bool(torch.isfinite(o).all())
+    rng = np.random.default_rng(501)
+    pairs = sorted({(int(rng.integers(0, B)), int(rng.integers(0, H))) for _ in range(40)} |
+                   {(int(np.argmax(kv.numpy())), 0), (int(np.argmin(kv.numpy())), H - 1)})
+    ref = _decode_ref(q, K, V, kv.numpy(), scale, pairs)
+    got = np.stack([to_np(o[b, h]) for b, h in pairs])
+    err = check_attention(got, ref, "decode full size")
+    print(f"decode: max abs err {err:.3e} over {len(pairs)} (b, h) pairs; kv_len={kv.tolist()}")
+
+
+# ---- merge_partials ----------------------------------------------------------
+
+def _merge_ref(m, l, O):
+    mo, lo, Oo = oracle.merge_direct(m.numpy(), l.numpy(), O.numpy())
+    with np.errstate(invalid="ignore", divide="ignore"):
+        on = np.where(lo[:, None] > 0, Oo / np.where(lo > 0, lo, 1.0)[:, None], 0.0)
+    return mo, lo, Oo, on
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 63, 64, 65, 200, 1024])
+@pytest.mark.parametrize("D", [1, 7, 8, 64, 128])
+def test_merge_parity(S, D):
+    say(f"merge S={S} D={D}")
+    N = 50
+    m, l, O = inputs.partials(N, S, D, seed=S * 131 + D, empty_frac=0.1)
+    o, mo, lo = tea.merge_partials(m.to(DEV), l.to(DEV), O.to(DEV), stats=True)
+    torch.cuda.synchronize()
+    mref, lref, _, oref = _merge_ref(m, l, O)
+    assert np.array_equal(to_np(mo).astype(np.float64), mref)
+    ok = lref > 0
+    assert np.all(np.abs(to_np(lo)[ok] - lref[ok]) <= 2e-5 * lref[ok])
+    assert np.all(to_np(lo)[~ok] == 0) and np.all(to_np(o)[~ok] == 0)
+    # fp32 weights exp(m_s - M) carry ~|m_s - M| * 2^-24 relative error; the
+    # partials here spread m over +-40, so 3e-5 of the row's magnitude
+    scale = np.maximum(np.abs(oref).max(axis=1, keepdims=True), 1.0)
+    assert np.max(np.abs(to_np(o) - oref) / scale) <= 3e-5
+
+
+def test_merge_unnormalised_bf16_and_identity():
+    say("merge unnormalised / bf16 / identity")
+    N, S, D = 40, 64, 128
+    m, l, O = inputs.partials(N, S, D, seed=77)
+    mref, lref, Oref, oref = _merge_ref(m, l, O)
+    u = tea.merge_partials(m.to(DEV), l.to(DEV), O.to(DEV), normalize=False)
+    b = tea.merge_partials(m.to(DEV), l.to(DEV), O.to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(to_np(u) - Oref) / np.abs(Oref).max(axis=1, keepdims=True)) <= 3e-5
+    check_attention(to_np(b), oref, "merge bf16")
+    # appending empty partials changes nothing, bitwise
+    e_m = torch.full((N, S), -math.inf)
+    e_l = torch.zeros((N, S))
+    e_O = torch.zeros((N, S, D))
+    m2 = torch.cat([m, e_m], 1)
+    l2 = torch.cat([l, e_l], 1)
+    O2 = torch.cat([O, e_O], 1)
+    a1 = tea.merge_partials(m.to(DEV), l.to(DEV), O.to(DEV))
+    a2 = tea.merge_partials(m2.to(DEV), l2.to(DEV), O2.to(DEV))
+    torch.cuda.synchronize()
+    # With 128 partials each lane first folds two ((identity, p), p'), which
+    # is the first tree level of the 64-partial merge; the upper 32 lanes
+    # hold only empty states, and combining with the empty state is exact.
+    assert torch.equal(a1, a2)
+    # all-empty rows
+    z, zm, zl = tea.merge_partials(e_m.to(DEV), e_l.to(DEV), e_O.to(DEV), stats=True)
+    torch.cuda.synchronize()
+    assert torch.all(z == 0) and torch.all(zm == -math.inf) and torch.all(zl == 0)
+
+
+def test_merge_tree_shapes_agree():
+    """Merging 64 partials at once, or as two merged halves merged again,
+    agrees up to rounding (the combine is associative)."""
+    say("merge tree shapes")
+    N, S, D = 30, 64, 64
+    m, l, O = (t.to(DEV) for t in inputs.partials(N, S, D, seed=78))
+    whole = tea.merge_partials(m, l, O)
+    halves = [tea.merge_partials(m[:, i:i + 32].contiguous(), l[:, i:i + 32].contiguous(),
+                                 O[:, i:i + 32].contiguous(), normalize=False, stats=True) for i in (0, 32)]
+    mm = torch.stack([h[1] for h in halves], 1)
+    ll = torch.stack([h[2] for h in halves], 1)
+    OO = torch.stack([h[0] for h in halves], 1)
+    again = tea.merge_partials(mm.contiguous(), ll.contiguous(), OO.contiguous())
+    torch.cuda.synchronize()
+    assert float((whole - again).abs().max()) <= 3e-5 * float(whole.abs().max())

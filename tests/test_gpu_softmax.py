@@ -1,0 +1,150 @@
+"""GPU parity of row_softmax against the fp64 two-pass oracle.
+
+Workloads: 4096 x 1024 fp32 logits N(0,1) x {1, 1000} in blocks of 8 and the
+64-logit vector ("The Online Softmax" (curionode), Workshop and One pass,
+exactly); 65536 x 8192 in fp32 and bf16 at scales {1, 30, 1000}, compared on
+sampled rows and by properties that hold at any size; ragged and tiny row
+lengths, every block size, empty rows and in-place operation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_amd as tea
+from tiled_exact_attention_amd import inputs
+from gpu_util import check_softmax, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _run(x_cpu: torch.Tensor, block=8):
+    x = x_cpu.to(DEV)
+    y, m, l = tea.row_softmax(x, block=block, stats=True)
+    torch.cuda.synchronize()
+    return y, m, l
+
+
+def _compare(x_cpu, y, m, l, rel, what):
+    xf = x_cpu.float().numpy()
+    ref, mref, lref = oracle.softmax_rows(xf)
+    e = check_softmax(to_np(y), ref, rel, what)
+    assert np.array_equal(to_np(m).astype(np.float64), mref), f"{what}: row maxima differ"
+    lr = np.max(np.abs(to_np(l) - lref) / lref)
+    assert lr <= 1e-5, f"{what}: normaliser relative error {lr:.2e}"
+    return e
+
+
+@pytest.mark.parametrize("scale,seed", [(1.0, 101), (1000.0, 102)])
+def test_small_config_full_parity(scale, seed):
+    say(f"row_softmax 4096x1024 f32 scale={scale}")
+    x = inputs.logits(4096, 1024, scale, seed, "f32")
+    y, m, l = _run(x, block=8)
+    e = _compare(x, y, m, l, 1e-5, f"4096x1024 x{scale}")
+    print(f"max rel err {e:.3e}")
+
+
+@pytest.mark.parametrize("scale,seed", [(1.0, 103), (1000.0, 104)])
+def test_vector64(scale, seed):
+    say(f"row_softmax 1x64 scale={scale}")
+    v = inputs.vector64(scale, seed).astype(np.float32)
+    x = torch.from_numpy(v.reshape(1, 64))
+    y, m, l = _run(x, block=8)
+    _compare(x, y, m, l, 1e-5, f"vector64 x{scale}")
+
+
+@pytest.mark.parametrize("cols", [1, 2, 7, 8, 9, 63, 64, 65, 255, 256, 257, 1000, 1024, 2047, 2048, 2049, 4097,
+                                  8191, 8192, 12345, 16384])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_cols(cols, dtype):
+    say(f"row_softmax cols={cols} {dtype}")
+    rows = 37
+    x = inputs.logits(rows, cols, 30.0, 1000 + cols, dtype)
+    y, m, l = _run(x)
+    _compare(x, y, m, l, 1e-5 if dtype == "f32" else 4e-3, f"cols={cols} {dtype}")
+
+
+@pytest.mark.parametrize("block", [0, 1, 2, 4, 8, 16, 32, 64])
+def test_block_sizes_agree(block):
+    say(f"row_softmax block={block}")
+    x = inputs.logits(64, 8192, 30.0, 7, "f32")
+    y, m, l = _run(x, block=block)
+    _compare(x, y, m, l, 1e-5, f"block={block}")
+    y8, _, _ = _run(x, block=8)
+    d = (to_np(y) - to_np(y8)) / np.maximum(to_np(y8), 2.0 ** -126)
+    assert np.max(np.abs(d)) <= 2e-5  # same result up to rounding
+
+
+def test_misaligned_rows_take_scalar_path():
+    say("row_softmax misaligned base pointer")
+    x_cpu = inputs.logits(33, 1024, 5.0, 8, "f32")
+    xs = torch.empty(33 * 1024 + 1, device=DEV)[1:].view(33, 1024)  # 4 bytes past 16-byte alignment
+    xs.copy_(x_cpu)
+    y, m, l = tea.row_softmax(xs, stats=True)
+    torch.cuda.synchronize()
+    _compare(x_cpu, y, m, l, 1e-5, "misaligned")
+
+
+def test_in_place_and_empty_and_all_neg_inf():
+    say("row_softmax in place / empty rows / -inf rows")
+    x_cpu = inputs.logits(16, 1024, 3.0, 9, "f32")
+    x_cpu[3] = -math.inf
+    x_cpu[5, :512] = -math.inf
+    x = x_cpu.to(DEV)
+    ref, mref, lref = oracle.softmax_rows(x_cpu.numpy())
+    y, m, l = tea.row_softmax(x, out=x, stats=True)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr()
+    check_softmax(to_np(y), ref, 1e-5, "in place")
+    assert np.all(to_np(y)[3] == 0.0) and to_np(m)[3] == -math.inf and to_np(l)[3] == 0.0
+    e = torch.empty((5, 0), device=DEV)
+    y0, m0, l0 = tea.row_softmax(e, stats=True)
+    torch.cuda.synchronize()
+    assert y0.shape == (5, 0) and torch.all(m0 == -math.inf) and torch.all(l0 == 0)
+    z = tea.row_softmax(torch.empty((0, 100), device=DEV))
+    assert z.shape == (0, 100)
+
+
+def test_deterministic():
+    say("row_softmax determinism")
+    x = inputs.logits(512, 8192, 30.0, 11, "bf16").to(DEV)
+    a = tea.row_softmax(x)
+    b = tea.row_softmax(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---- 65536 x 8192, the bandwidth-bound workload, at full size ----------------
+
+SAMPLE = np.unique(np.concatenate([np.arange(0, 65536, 1024), np.arange(0, 64), np.arange(65536 - 64, 65536),
+                                   np.random.default_rng(5).integers(0, 65536, 64)]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 30.0, 1000.0])
+def test_large_config_full_size(dtype, scale):
+    seed = 201 + (0 if dtype == "f32" else 3) + [1.0, 30.0, 1000.0].index(scale)
+    say(f"row_softmax 65536x8192 {dtype} x{scale} (seed {seed})")
+    x_cpu = inputs.logits(65536, 8192, scale, seed, dtype)
+    x = x_cpu.to(DEV)
+    y, m, l = tea.row_softmax(x, stats=True)
+    torch.cuda.synchronize()
+    # every row: finite, in [0, 1], sums to 1 within the elementwise bound
+    # (fp32: 1e-5 relative per term; bf16: 2^-9 rounding per term), maxima
+    # exact
+    assert bool(torch.isfinite(y).all()) and bool((y >= 0).all()) and bool((y <= 1).all())
+    for r0 in range(0, 65536, 8192):
+        s = y[r0:r0 + 8192].double().sum(dim=1)
+        assert float((s - 1).abs().max()) <= (2e-5 if dtype == "f32" else 4e-3)
+    assert torch.equal(m, x.float().amax(dim=1))
+    assert bool(torch.isfinite(l).all()) and bool((l >= 1).all())
+    # sampled rows against the oracle, element by element
+    idx = torch.from_numpy(SAMPLE)
+    xs = x_cpu[idx]
+    _compare(xs, y.cpu()[idx], m.cpu()[idx], l.cpu()[idx], 1e-5 if dtype == "f32" else 4e-3,
+             f"65536x8192 {dtype} x{scale}")
+    del x, y

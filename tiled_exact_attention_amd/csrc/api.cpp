@@ -1,0 +1,146 @@
+// C ABI of libtea.so: argument validation (before any HIP call) and dispatch
+// to the kernels.  See include/tea.h for the contract of each entry point.
+#include "tea.h"
+
+#include <math.h>
+
+#include "launch.hpp"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (bytes)
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? TEA_OK : TEA_EHIP; }
+
+inline bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+int tea_abi_version(void) { return 1; }
+
+const char* tea_status_string(int status)
+{
+    switch (status) {
+    case TEA_OK: return "ok";
+    case TEA_EINVAL: return "invalid argument";
+    case TEA_EUNSUPPORTED: return "unsupported configuration";
+    case TEA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, float* m_out,
+                float* l_out, void* stream)
+{
+    if (rows < 0 || cols < 0) return TEA_EINVAL;
+    if (dtype != TEA_F32 && dtype != TEA_BF16) return TEA_EINVAL;
+    if (block < 0) return TEA_EINVAL;
+    if (block == 0) block = 8;
+    if (block > 32) block = 32;
+    if (block & (block - 1)) return TEA_EUNSUPPORTED;
+    if (rows == 0) return TEA_OK;
+    if (cols > tea::row_softmax_max_cols()) return TEA_EUNSUPPORTED;
+    if (rows > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;  // grid limit (one row per workgroup at most)
+    const size_t es = dtype == TEA_F32 ? 4 : 2;
+    if (cols > 0) {
+        if (!x || !y) return TEA_EINVAL;
+        if (!aligned(x, es) || !aligned(y, es)) return TEA_EINVAL;
+        const size_t bytes = (size_t)rows * (size_t)cols * es;
+        if (x != y && overlap(x, bytes, y, bytes)) return TEA_EINVAL;
+    }
+    if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4))) return TEA_EINVAL;
+    tea::RowSoftmaxArgs a{x, y, rows, cols, dtype == TEA_BF16, block, m_out, l_out, (hipStream_t)stream};
+    return status_of(tea::launch_row_softmax(a));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq, int Sk, int D,
+             float scale, int causal, int out_dtype, float* lse_out, void* stream)
+{
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (causal != 0 && causal != 1) return TEA_EINVAL;
+    if (!good_scale(scale)) return TEA_EINVAL;
+    if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
+    if (causal && Sq != Sk) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H * Sq == 0) return TEA_OK;
+    if ((int64_t)B * H * ((Sq + 127) / 128) > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if (!q || !o || (Sk > 0 && (!k || !v))) return TEA_EINVAL;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return TEA_EINVAL;
+    if (lse_out && !aligned(lse_out, 4)) return TEA_EINVAL;
+    const size_t qb = (size_t)B * H * Sq * D * 2, kb = (size_t)B * H * Sk * D * 2;
+    const size_t ob = (size_t)B * H * Sq * D * (out_dtype == TEA_F32 ? 4 : 2);
+    if (overlap(o, ob, q, qb) || (Sk > 0 && (overlap(o, ob, k, kb) || overlap(o, ob, v, kb)))) return TEA_EINVAL;
+    if (lse_out && overlap(lse_out, (size_t)B * H * Sq * 4, o, ob)) return TEA_EINVAL;
+    tea::AttnArgs a{q, k, v, o, B, H, Sq, Sk, D, scale, causal == 1, out_dtype == TEA_BF16, lse_out,
+                    (hipStream_t)stream};
+    return status_of(tea::launch_attn_fwd(a));
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int D, int num_splits)
+{
+    if (B < 0 || H < 0 || D <= 0 || num_splits < 1 || num_splits > 1024) return 0;
+    return tea::decode_workspace_bytes(B, H, D, num_splits);
+}
+
+int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B,
+                        int H, int Lmax, int D, int num_splits, float scale, int out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || H < 0 || Lmax < 1 || D <= 0) return TEA_EINVAL;
+    if (num_splits < 1 || num_splits > 1024) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (!good_scale(scale)) return TEA_EINVAL;
+    if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H == 0) return TEA_OK;
+    if ((int64_t)B * H * num_splits > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if (!q || !k || !v || !kv_len || !o || !workspace) return TEA_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(o, 4) ||
+        !aligned(workspace, 16))
+        return TEA_EINVAL;
+    const size_t need = tea::decode_workspace_bytes(B, H, D, num_splits);
+    if (workspace_bytes < need) return TEA_EINVAL;
+    const size_t ob = (size_t)B * H * D * (out_dtype == TEA_F32 ? 4 : 2);
+    if (overlap(workspace, need, o, ob)) return TEA_EINVAL;
+    const size_t n = (size_t)B * H * num_splits;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = static_cast<char*>(workspace);
+    float* ws_m = reinterpret_cast<float*>(ws);
+    float* ws_l = reinterpret_cast<float*>(ws + up(n * 4));
+    float* ws_O = reinterpret_cast<float*>(ws + 2 * up(n * 4));
+    tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, ws_m, ws_l,
+                      ws_O, (hipStream_t)stream};
+    return status_of(tea::launch_decode(a));
+}
+
+int merge_partials(const float* m, const float* l, const float* O, int64_t N, int S, int D, float* m_out,
+                   float* l_out, void* O_out, int out_dtype, int normalize, void* stream)
+{
+    if (N < 0 || S < 1 || S > 65536 || D < 1 || D > 4096) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (normalize != 0 && normalize != 1) return TEA_EINVAL;
+    if (!normalize && out_dtype != TEA_F32) return TEA_EINVAL;
+    if (N == 0) return TEA_OK;
+    if (N * ((D + 7) / 8) > (int64_t)0x7fffffff * 4) return TEA_EUNSUPPORTED;
+    if (!m || !l || !O || !O_out) return TEA_EINVAL;
+    if (!aligned(m, 4) || !aligned(l, 4) || !aligned(O, 4) || !aligned(O_out, out_dtype == TEA_F32 ? 4 : 2))
+        return TEA_EINVAL;
+    if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4))) return TEA_EINVAL;
+    const size_t ob = (size_t)N * D * (out_dtype == TEA_F32 ? 4 : 2);
+    if (overlap(O_out, ob, O, (size_t)N * S * D * 4) || overlap(O_out, ob, m, (size_t)N * S * 4) ||
+        overlap(O_out, ob, l, (size_t)N * S * 4))
+        return TEA_EINVAL;
+    tea::MergeArgs a{m, l, O, N, S, D, m_out, l_out, O_out, out_dtype == TEA_BF16, normalize == 1,
+                     (hipStream_t)stream};
+    return status_of(tea::launch_merge(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Split-KV decode: one query token per (batch, head) against a ragged KV
+// cache, split into num_splits contiguous chunks whose partial softmax states
+// (m, l, O) are merged by the associative combine ("The Online Softmax"
+// (curionode), One pass, exactly; "Online Softmax" (metalworking),
+// Recognition guide: split-KV decode kernels merge partials with the same
+// correction, with no float atomics).
+//
+// Launch 1 (this file): one workgroup per (b, h, chunk).  Chunk c of a
+// sequence of L keys covers keys [floor(c L / S), floor((c+1) L / S)), so
+// chunks are empty when L < S.  Each lane group of D/8 lanes owns one key slot
+// and a slice of 8 dimensions; per step a slot takes U keys, computes their
+// scores (DPP reduction across the group), and folds them into its running
+// (m, l, O) with the online recurrence.  The slots' states are merged inside
+// the wave, the four waves' states through LDS, and the chunk's state is
+// written to the workspace (maxima in base-two units, O unnormalised).
+// K and V are read from HBM exactly once.
+// Launch 2 (merge.hip): a tree merge of the num_splits partials per (b, h).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace tea {
+
+hipError_t launch_merge_base2(const MergeArgs& a);
+
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int D>
+__device__ __forceinline__ float group_sum(float v)
+{
+    // sum over the D/8 lanes of one key slot
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    if constexpr (D == 128) v += dpp_f<0x140>(v);
+    return v;
+}
+
+// (m1, l1, O1) <- combine((m1, l1, O1), (m2, l2, O2)), base-two maxima.
+__device__ __forceinline__ void combine8(float& m1, float& l1, float* O1, float m2, float l2, const float* O2)
+{
+    const float m = fmaxf(m1, m2);
+    const float mu = guard_max(m);
+    const float a1 = exp2_hw(m1 - mu), a2 = exp2_hw(m2 - mu);
+    l1 = fmaf(a1, l1, a2 * l2);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) O1[d] = fmaf(a1, O1[d], a2 * O2[d]);
+    m1 = m;
+}
+
+template <int D, int U>
+__global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             const int32_t* __restrict__ kv_len, int H, int Lmax,
+                                                             int S, float scale_log2, float* __restrict__ ws_m,
+                                                             float* __restrict__ ws_l, float* __restrict__ ws_O)
+{
+    constexpr int LPK = D / 8;       // lanes per key
+    constexpr int KPW = 64 / LPK;    // key slots per wave
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int slot = lane / LPK, dl = lane % LPK;
+    const int64_t bid = blockIdx.x;
+    const int c = (int)(bid % S);
+    const int64_t bh = bid / S;
+    const int b = (int)(bh / H);
+    int L = kv_len[b];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int64_t k0 = (int64_t)c * L / S, k1 = (int64_t)(c + 1) * L / S;
+
+    // q with scale * log2(e) folded in once: scores come out in base two
+    float qs[8];
+    {
+        const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(q + bh * D + dl * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qs[2 * j] = bf16_lo(w4[j]) * scale_log2;
+            qs[2 * j + 1] = bf16_hi(w4[j]) * scale_log2;
+        }
+    }
+    const uint16_t* kb = k + bh * (int64_t)Lmax * D + dl * 8;
+    const uint16_t* vb = v + bh * (int64_t)Lmax * D + dl * 8;
+
+    float m = kNegInf, l = 0.0f, O[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) O[d] = 0.0f;
+
+    constexpr int STEP = kWaves * U * KPW;  // keys per workgroup step
+    for (int64_t base = k0 + (int64_t)w * U * KPW; base < k1; base += STEP) {
+        u32x4_t kr[U], vr[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t key = base + u * KPW + slot;
+            ok[u] = key < k1;
+            key = ok[u] ? key : k1 - 1;  // in bounds; its score is masked below
+            kr[u] = *reinterpret_cast<const u32x4_t*>(kb + key * D);
+            vr[u] = *reinterpret_cast<const u32x4_t*>(vb + key * D);
+        }
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc = fmaf(qs[2 * j], bf16_lo(kr[u][j]), acc);
+                acc = fmaf(qs[2 * j + 1], bf16_hi(kr[u][j]), acc);
+            }
+            acc = group_sum<D>(acc);
+            s[u] = ok[u] ? acc : kNegInf;
+        }
+        float bm = s[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) bm = fmaxf(bm, s[u]);
+        const float mn = fmaxf(m, bm);
+        const float mu = guard_max(mn);
+        const float corr = exp2_hw(m - mu);
+        float ps = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) O[d] *= corr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = exp2_hw(s[u] - mu);
+            ps += p;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                O[2 * j] = fmaf(p, bf16_lo(vr[u][j]), O[2 * j]);
+                O[2 * j + 1] = fmaf(p, bf16_hi(vr[u][j]), O[2 * j + 1]);
+            }
+        }
+        l = fmaf(l, corr, ps);
+        m = mn;
+    }
+
+    // merge the key slots of this wave (butterfly over lane groups)
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) {
+        float mp = __shfl_xor(m, x), lp = __shfl_xor(l, x), Op[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) Op[d] = __shfl_xor(O[d], x);
+        if (lane & x) {
+            float Om[8], mm = m, lm = l;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                Om[d] = O[d];
+                O[d] = Op[d];
+            }
+            m = mp;
+            l = lp;
+            combine8(m, l, O, mm, lm, Om);
+        } else {
+            combine8(m, l, O, mp, lp, Op);
+        }
+    }
+
+    // merge the four waves: a balanced tree ((w0, w1), (w2, w3))
+    __shared__ float sm[kWaves], sl[kWaves], sO[kWaves][D];
+    if (lane < LPK) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) sO[w][dl * 8 + d] = O[d];
+        if (lane == 0) {
+            sm[w] = m;
+            sl[w] = l;
+        }
+    }
+    __syncthreads();
+    if (w == 0 && lane < LPK) {
+        float m0 = sm[0], l0 = sl[0], m2 = sm[2], l2 = sl[2], O0[8], O1[8], O2[8], O3[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            O0[d] = sO[0][dl * 8 + d];
+            O1[d] = sO[1][dl * 8 + d];
+            O2[d] = sO[2][dl * 8 + d];
+            O3[d] = sO[3][dl * 8 + d];
+        }
+        combine8(m0, l0, O0, sm[1], sl[1], O1);
+        combine8(m2, l2, O2, sm[3], sl[3], O3);
+        combine8(m0, l0, O0, m2, l2, O2);
+        const int64_t p = bh * S + c;
+        if (lane == 0) {
+            ws_m[p] = m0;
+            ws_l[p] = l0;
+        }
+        f32x4v_t* dst = reinterpret_cast<f32x4v_t*>(ws_O + p * D + dl * 8);
+        dst[0] = f32x4v_t{O0[0], O0[1], O0[2], O0[3]};
+        dst[1] = f32x4v_t{O0[4], O0[5], O0[6], O0[7]};
+    }
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int H, int D, int num_splits)
+{
+    const size_t n = (size_t)B * H * num_splits;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return 2 * up(n * sizeof(float)) + up(n * D * sizeof(float));
+}
+
+hipError_t launch_decode(const DecodeArgs& a)
+{
+    const int64_t grid = (int64_t)a.B * a.H * a.num_splits;
+    const float scale_log2 = a.scale * kLog2eHi;
+    if (a.D == 128)
+        hipLaunchKernelGGL((decode_partial_kernel<128, 4>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, a.H, a.Lmax,
+                           a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, a.H, a.Lmax,
+                           a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MergeArgs m{a.ws_m, a.ws_l, a.ws_O, (int64_t)a.B * a.H, a.num_splits, a.D, nullptr, nullptr, a.o, a.out_bf16,
+                true, a.stream};
+    return launch_merge_base2(m);
+}
+
+}  // namespace tea
