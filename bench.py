@@ -64,6 +64,65 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) that make up one launch
+    "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256>"],
+    "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
+    "attn_nc": ["attn_fwd_kernel<64, false, true>"],
+    "attn_causal": ["attn_fwd_kernel<128, true, true>"],
+    "decode": ["decode_partial_kernel<128, 4>", "merge_kernel<true, true, true>"],
+}
+STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
+                "attn_causal": "attn_fwd", "decode": "decode"}
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, command: str):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch of each stage, each counter scaled by
+    what it reads for the plain 1 GiB device copy of --calibrate-copy, and
+    write profiles/traffic.json (keyed by stage, with the hash of the
+    kernel sources the counters were taken with)."""
+    import csv
+    from collections import defaultdict
+
+    def load(path):
+        per = defaultdict(list)
+        copy = None
+        for r in csv.DictReader(open(path)):
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
+                copy = v
+            per[name].append(v)
+        return per, copy
+
+    fetch, fcopy = load(fetch_csv)
+    write, wcopy = load(write_csv)
+    gib_kib = float(1 << 20)
+    rf, wf = gib_kib / fcopy, gib_kib / wcopy
+    out = {"_calibration": {"copy_bytes": 1 << 30, "fetch_kib": fcopy, "write_kib": wcopy,
+                            "read_factor": rf, "write_factor": wf, "command": command}}
+    for stage, parts in STAGE_KERNELS.items():
+        fk = wk = 0.0
+        found = True
+        for sub in parts:
+            fn = [k for k in fetch if sub in k]
+            wn = [k for k in write if sub in k]
+            if not fn or not wn:
+                found = False
+                break
+            fv, wv = fetch[fn[0]], write[wn[0]]
+            fk += sum(fv) / len(fv)
+            wk += sum(wv) / len(wv)
+        if not found:
+            continue
+        out[stage] = {"source_hash": source_hash(STAGE_SOURCE[stage]), "fetch_kib": round(fk, 1),
+                      "write_kib": round(wk, 1), "read_bytes": int(fk * 1024 * rf),
+                      "write_bytes": int(wk * 1024 * wf), "bytes_per_launch": int(fk * 1024 * rf + wk * 1024 * wf)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
@@ -79,7 +138,14 @@ def main():
     ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--ingest-command", default="", help="the rocprofv3 command the counter files came from")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        print(json.dumps(ingest_counters(*args.ingest_counters, args.ingest_command), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

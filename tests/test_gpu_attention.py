@@ -1,6 +1,11 @@
 """GPU parity of attn_fwd against the fp64 oracle (attention from its
 definition).
 
+The log-sum-exp output is m + ln(l) with l summed from the same bf16-rounded
+weights that multiply V (so that it stays consistent with O for a merge of
+partial outputs); rounding each weight moves l by at most 2^-9 relative, so
+ln(l) by at most log(1 + 2^-9) < 1.96e-3: the tolerance is 2.5e-3.
+
 Workloads: non-causal B4 H16 S2048 D64 and causal B2 H32 S8192 D128, bf16
 N(0,1), scale 1/sqrt(D), at full size on sampled query rows; small shapes in
 full, spanning several tiles with ragged tails; closed forms that hold
@@ -21,6 +26,7 @@ from gpu_util import check_attention, say, to_np
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+LSE_TOL = 2.5e-3
 
 
 def _np32(t):
@@ -45,7 +51,7 @@ def test_small_full_parity(D, causal, S):
     o, lse, scale = _run(q, k, v, causal)
     O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal)
     check_attention(to_np(o), O, f"S={S} D={D} causal={causal}")
-    assert np.max(np.abs(to_np(lse) - L)) <= 1e-3
+    assert np.max(np.abs(to_np(lse) - L)) <= LSE_TOL
 
 
 @pytest.mark.parametrize("Sq,Sk", [(1, 1000), (100, 1), (129, 65), (64, 1000), (333, 2049)])
@@ -55,7 +61,7 @@ def test_noncausal_rectangular(Sq, Sk):
     o, lse, scale = _run(q, k, v, False)
     O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, False)
     check_attention(to_np(o), O, f"Sq={Sq} Sk={Sk}")
-    assert np.max(np.abs(to_np(lse) - L)) <= 1e-3
+    assert np.max(np.abs(to_np(lse) - L)) <= LSE_TOL
 
 
 def test_fp32_output():
@@ -133,5 +139,5 @@ def test_full_size_sampled(cfg):
     O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal, rows=rows)
     got = o.reshape(-1, D).cpu()[torch.from_numpy(rows)]
     err = check_attention(to_np(got), O, cfg)
-    assert np.max(np.abs(to_np(lse).reshape(-1)[rows] - L)) <= 1e-3
+    assert np.max(np.abs(to_np(lse).reshape(-1)[rows] - L)) <= LSE_TOL
     print(f"{cfg}: max abs err {err:.3e} over {len(rows)} sampled rows")
