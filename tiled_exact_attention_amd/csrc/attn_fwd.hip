@@ -102,20 +102,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     u32x4_t kreg[KPT], vreg[4];
     const int vkg = tid % VKG, vdc = tid / VKG;  // V: keys 4*vkg.., dims 8*vdc..
 
+    // per-thread element offsets of the staged chunks inside a tile
+    int koff[KPT], voff[4];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = tid + 256 * j;
+        koff[j] = (i / KCH) * D + (i % KCH) * 8;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) voff[r] = (4 * vkg + r) * D + vdc * 8;
+
     auto gload = [&](int t) {
         const int key0 = t * BN;
+        const uint16_t* kt = kp + (int64_t)key0 * D;
+        const uint16_t* vt = vp + (int64_t)key0 * D;
+        if (key0 + BN <= Sk) {  // full tile: no per-chunk test (uniform branch)
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int i = tid + 256 * j;
-            const int key = key0 + i / KCH;
-            kreg[j] = key < Sk ? *reinterpret_cast<const u32x4_t*>(kp + (int64_t)key * D + (i % KCH) * 8)
-                               : u32x4_t{0u, 0u, 0u, 0u};
-        }
+            for (int j = 0; j < KPT; ++j) kreg[j] = *reinterpret_cast<const u32x4_t*>(kt + koff[j]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * vkg + r;
-            vreg[r] = key < Sk ? *reinterpret_cast<const u32x4_t*>(vp + (int64_t)key * D + vdc * 8)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+            for (int r = 0; r < 4; ++r) vreg[r] = *reinterpret_cast<const u32x4_t*>(vt + voff[r]);
+        } else {  // ragged last tile: rows past Sk read row Sk - 1 and are zeroed
+            const int nvalid = Sk - key0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int row = (tid + 256 * j) / KCH;
+                const int off = row < nvalid ? koff[j] : koff[j] - (row - nvalid + 1) * D;
+                const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kt + off);
+                kreg[j] = row < nvalid ? x : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * vkg + r;
+                const int off = row < nvalid ? voff[r] : voff[r] - (row - nvalid + 1) * D;
+                const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vt + off);
+                vreg[r] = row < nvalid ? x : u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
     };
     auto lds_store = [&](int buf) {
