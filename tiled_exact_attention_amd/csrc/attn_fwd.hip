@@ -4,8 +4,8 @@
 // (curionode), One pass, exactly: blocks stream through fast memory and no
 // row of scores is ever stored).
 //
-// Workgroup: 4 waves, 128 queries (32 per wave); KV tiles of BN keys (64 for
-// D = 128, 128 for D = 64) double-buffered in LDS.  Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
+// Workgroup: 4 waves, 128 queries (32 per wave); KV tiles of 64 keys
+// double-buffered in LDS.  Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
 //     S^T = K Q^T   (A = K tile from LDS, B = Q^T held in registers)
 //     O^T = V^T P^T (A = V^T tile from LDS, B = P^T straight from the S^T
 //                    accumulators)
@@ -22,6 +22,8 @@
 // correction alpha too); m starts at -inf and l at 0; a row whose keys in a
 // tile are all masked keeps -inf out of every exponent through the guard
 // ("Online softmax", Initialise honestly and Things that break).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,31 +33,67 @@ namespace {
 
 constexpr int kBM = 128;  // queries per workgroup (4 waves x 32)
 
-// Position of key (4*kg .. 4*kg+3) inside its 16-key chunk of the V^T tile:
-// keys 16c + 4a + r sit at 16c + {0, 8, 4, 12}[a] + r, which is the order in
-// which the S^T accumulator registers of one lane half hold them.
-__device__ __forceinline__ int vt_pos(int kg) { return 16 * (kg >> 2) + ((kg & 1) << 3) + ((kg & 2) << 1); }
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
 
-// D: head dimension; BN: keys per KV tile.  Two waves per SIMD (at most 256
-// registers each) so that one wave's exponentials overlap the other's MFMAs.
-template <int D, int BN, bool CAUSAL, bool OUT_BF16>
+// Tiles live in LDS row-major (one key per row, D contiguous bf16), without
+// padding, because they are filled by direct HBM->LDS loads that write 1 KiB
+// contiguously per wave.  Bank conflicts are avoided instead by XOR-swizzling
+// the 16-byte chunks of each row:
+//   K rows are read 16 bytes per lane, 16 lanes (16 consecutive rows) per
+//   LDS cycle: chunk ^ (row % 16) (D = 128) or chunk ^ ((row / 2) % 8)
+//   (D = 64, two rows share the 64 banks) puts those 16 reads on distinct
+//   banks;
+//   V rows are read by the transposing ds_read_b64_tr_b16, 32 lanes covering
+//   4 rows x 8 half-chunks: chunk ^ 4 * (row % 4) (D = 128) or
+//   chunk ^ 4 * ((row / 2) % 2) (D = 64) spreads them over all 64 banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row)
+{
+    if constexpr (D == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row)
+{
+    if constexpr (D == 128) return (row & 3) << 2;
+    else return ((row >> 1) & 1) << 2;
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// D: head dimension; BN: keys per KV tile.  Two waves per SIMD.
+//
+// Software pipeline: K runs one tile ahead of V.  Iteration t issues the HBM
+// loads of V(t) and K(t+2), then the MFMAs of O += V(t-1)^T P(t-1) next to the
+// exponentials of tile t, then the MFMAs of S(t+1) = K(t+1) Q^T next to the
+// rescale of O by alpha(t); the two halves of each pair are independent, so
+// the matrix cores and the vector ALUs work at the same time.  The rescale is
+// unconditional (multiplying by exactly 1 where a row's maximum did not rise),
+// which the pages show as the MLX form ("Online Softmax" (metalworking),
+// Recognition guide); it runs under the S MFMAs.
+template <int D, int BN, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, void* __restrict__ o,
-                                                          float* __restrict__ lse, int Sq, int Sk, float c, int nqb)
+                                                          float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal)
 {
-    constexpr int KST = D + 8;             // K tile row stride (elements), padded against bank conflicts
-    constexpr int VST = BN + 8;            // V^T tile row stride
-    constexpr int KCH = D / 8;             // 16-byte chunks per K/V row
-    constexpr int KPT = BN * KCH / 256;    // K chunks staged per thread
-    constexpr int NKB = BN / 32;           // 32-key blocks of S^T
-    constexpr int NC4 = BN / 16;           // 16-key chunks of P^T
-    constexpr int NDB = D / 32;            // 32-wide dimension blocks of O^T
-    constexpr int NQC = D / 16;            // 16-wide contraction chunks of Q K^T
-    constexpr int VKG = BN / 4;            // key groups of 4 in a tile
-    static_assert(VKG * KCH == 256, "one 4-key x 8-dim V block per thread");
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KST];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VST];
+    // causal is a runtime flag: as a template parameter it made hipcc spill
+    // the non-causal instantiation
+    const bool CAUSAL = causal != 0;
+    constexpr int TILE = BN * D;                  // elements per K or V tile (16 KiB)
+    constexpr int NCH = D / 8;                    // 16-byte chunks per row
+    constexpr int RPI = 1024 / (2 * D);           // rows one wave-wide 16-byte-per-lane load fills
+    constexpr int DPW = TILE * 2 / 1024 / 4;      // such loads per wave per tile
+    constexpr int NKB = BN / 32;                  // 32-key blocks of S^T
+    constexpr int NC4 = BN / 16;                  // 16-key chunks of P^T
+    constexpr int NDB = D / 32;                   // 32-wide dimension blocks of O^T
+    constexpr int NQC = D / 16;                   // 16-wide contraction chunks of Q K^T
+    static_assert(DPW * 4 * RPI == BN, "tile rows must split evenly over the waves");
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lq = lane & 31, h = lane >> 5;
@@ -72,8 +110,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const int qrow = q0 + w * 32 + lq;
 
     const uint16_t* qp = q + bh * (int64_t)Sq * D;
-    const uint16_t* kp = k + bh * (int64_t)Sk * D;
-    const uint16_t* vp = v + bh * (int64_t)Sk * D;
+    const char* kp = reinterpret_cast<const char*>(k + bh * (int64_t)Sk * D);
+    const char* vp = reinterpret_cast<const char*>(v + bh * (int64_t)Sk * D);
 
     // Q^T operand: lane (query lq, half h) holds Q[q][16c + 8h .. +8)
     bf16x8_t qop[NQC];
@@ -98,166 +136,245 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     const int kend = CAUSAL ? (Sk < q0 + kBM ? Sk : q0 + kBM) : Sk;
     const int ntiles = (kend + BN - 1) / BN;
 
-    // staging registers: the next tile's K chunks and one 4-key x 8-dim V block
-    u32x4_t kreg[KPT], vreg[4];
-    const int vkg = tid % VKG, vdc = tid / VKG;  // V: keys 4*vkg.., dims 8*vdc..
-
-    // per-thread element offsets of the staged chunks inside a tile
-    int koff[KPT], voff[4];
+    // ---- HBM -> LDS: lane `lane` of this wave's j-th load fills 16 bytes
+    // at byte (w * DPW + j) * 1024 + 16 * lane of the tile, i.e. row
+    // drow[j], physical chunk lane % NCH, which holds logical chunk
+    // (lane % NCH) ^ swizzle(row).
+    auto dma = [&](const char* src, uint16_t* tile, bool is_v, int key0) {
+        const char* g = src + (int64_t)key0 * 2 * D;
+        const int nvalid = Sk - key0;  // >= 1 for every tile loaded
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int i = tid + 256 * j;
-        koff[j] = (i / KCH) * D + (i % KCH) * 8;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = (4 * vkg + r) * D + vdc * 8;
-
-    auto gload = [&](int t) {
-        const int key0 = t * BN;
-        const uint16_t* kt = kp + (int64_t)key0 * D;
-        const uint16_t* vt = vp + (int64_t)key0 * D;
-        if (key0 + BN <= Sk) {  // full tile: no per-chunk test (uniform branch)
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) kreg[j] = *reinterpret_cast<const u32x4_t*>(kt + koff[j]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vreg[r] = *reinterpret_cast<const u32x4_t*>(vt + voff[r]);
-        } else {  // ragged last tile: rows past Sk read row Sk - 1 and are zeroed
-            const int nvalid = Sk - key0;
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const int row = (tid + 256 * j) / KCH;
-                const int off = row < nvalid ? koff[j] : koff[j] - (row - nvalid + 1) * D;
-                const u32x4_t x = *reinterpret_cast<const u32x4_t*>(kt + off);
-                kreg[j] = row < nvalid ? x : u32x4_t{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 4 * vkg + r;
-                const int off = row < nvalid ? voff[r] : voff[r] - (row - nvalid + 1) * D;
-                const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vt + off);
-                vreg[r] = row < nvalid ? x : u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto lds_store = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int i = tid + 256 * j;
-            *reinterpret_cast<u32x4_t*>(&sK[buf][(i / KCH) * KST + (i % KCH) * 8]) = kreg[j];
-        }
-        // transpose the 4 x 8 block: row d of V^T gets the 4 keys' values
-        const int pos = vt_pos(vkg);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {  // dims 8*vdc + 2jj (lo halves) and + 2jj + 1 (hi halves)
-            const unsigned a0 = __builtin_amdgcn_perm(vreg[1][jj], vreg[0][jj], 0x05040100u);
-            const unsigned a1 = __builtin_amdgcn_perm(vreg[3][jj], vreg[2][jj], 0x05040100u);
-            const unsigned b0 = __builtin_amdgcn_perm(vreg[1][jj], vreg[0][jj], 0x07060302u);
-            const unsigned b1 = __builtin_amdgcn_perm(vreg[3][jj], vreg[2][jj], 0x07060302u);
-            const int d = 8 * vdc + 2 * jj;
-            *reinterpret_cast<u32x2_t*>(&sV[buf][d * VST + pos]) = u32x2_t{a0, a1};
-            *reinterpret_cast<u32x2_t*>(&sV[buf][(d + 1) * VST + pos]) = u32x2_t{b0, b1};
+        for (int j = 0; j < DPW; ++j) {
+            const int row = (w * DPW + j) * RPI + lane / NCH;
+            const int phys = lane % NCH;
+            const int chunk = phys ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+            // rows past the sequence end repeat the last valid row (its scores
+            // are masked, its values meet P = 0)
+            const int srow = row < nvalid ? row : nvalid - 1;
+            __builtin_amdgcn_global_load_lds((gptr_t)(g + srow * 2 * D + (chunk << 4)),
+                                             (lptr_t)(tile + (w * DPW + j) * 512), 16, 0, 0);
         }
     };
 
-    // Two LDS buffers: tile t is read from buffer t % 2 while tile t + 1 is
-    // written to the other one and tile t + 2 is in flight from HBM/L2.
-    if (ntiles > 0) {
-        gload(0);
-        lds_store(0);
-        if (ntiles > 1) gload(1);
-    }
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        const int key0 = t * BN;
-        // a wave skips tiles entirely above its diagonal
-        if (!(CAUSAL && key0 > q0 + w * 32 + 31)) {
-            // ---- S^T = K Q^T ---------------------------------------------
-            f32x16_t sacc[NKB];
+    // ---- LDS -> registers ---------------------------------------------------
+    // K operand: row kb*32 + lq, logical chunk 2cc + h.  The swizzle depends
+    // on the row only through lq, so each lane keeps one byte offset per cc
+    // and kb adds a constant.
+    const int kswz = k_swz<D>(lq);
+    int kro[NQC];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+    for (int cc = 0; cc < NQC; ++cc) kro[cc] = (lq * D + (((2 * cc + h) ^ kswz) << 3)) * 2;
+    auto compute_s = [&](const uint16_t* kt, f32x16_t* sacc) {
+        const char* kb8 = reinterpret_cast<const char*>(kt);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+            for (int cc = 0; cc < NQC; ++cc) {
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb8 + kro[cc] + kb * 32 * D * 2);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[cc], sacc[kb], 0, 0, 0);
+            }
+        }
+    };
+    // V^T operand via ds_read_b64_tr_b16: in each 16-lane group g, lane
+    // s = a + 4 kk points at row 16 c4 + 8 r + 4 h + kk, dims
+    // 32 db + 16 (g % 2) + 4 a .. +4; the transposing read then hands lane
+    // 16 g + j the values of dim 32 db + 16 (g % 2) + j for those four rows,
+    // which are the keys P^T holds at contraction positions 8 h + 4 r .. +4.
+    // The swizzle bits depend on the row only through 4 h + kk, so each lane
+    // keeps one byte offset per db and (c4, r) add constants.
+    int vro[NDB];
+    {
+        const int grp = lane >> 4, sl = lane & 15;
+        const int vk = sl >> 2, va = sl & 3;
+        const int vrow0 = 4 * h + vk;
+        const int vchunk = 2 * (grp & 1) + (va >> 1);
+        const int vswz = v_swz<D>(vrow0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vro[db] = (vrow0 * D + (((4 * db + vchunk) ^ vswz) << 3) + ((va & 1) << 2)) * 2;
+    }
+    auto pv_one = [&](const char* vt8, const bf16x8_t* pop, int db, int c4) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + 16 * c4 * D * 2));
+        const s16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + (16 * c4 + 8) * D * 2));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[c4], oacc[db], 0, 0, 0);
+    };
+    auto pv = [&](const uint16_t* vt, const bf16x8_t* pop) {
+        const char* vt8 = reinterpret_cast<const char*>(vt);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c4 = 0; c4 < NC4; ++c4) pv_one(vt8, pop, db, c4);
+    };
+
+    // operand of the i-th PV MFMA (db = i / NC4, c4 = i % NC4) and of the
+    // i-th QK MFMA (kb = i / NQC, cc = i % NQC)
+    auto vread = [&](const char* vt8, int i) -> bf16x8_t {
+        const int db = i / NC4, c4 = i % NC4;
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + 16 * c4 * D * 2));
+        const s16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + (16 * c4 + 8) * D * 2));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto kread = [&](const char* kt8, int i) -> bf16x8_t {
+        const int kb = i / NQC, cc = i % NQC;
+        return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[cc] + kb * 32 * D * 2);
+    };
+
+    f32x16_t sacc[NKB];
+    bf16x8_t pprev[NC4];
+    unsigned pw[NKB * 8];  // P of the current tile as 32-bit words (pairs of bf16), assembled into pprev
+    constexpr int NPAIR = NKB * 8;  // pairs of S^T values per lane
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // P for one pair of S^T values: exponentials, rounding to bf16 (the pair
+    // becomes one 32-bit word of the P^T operand) and their sum into rs.
+    // The dot2 operand is the freshly rounded pair itself: hipcc (ROCm 7.2)
+    // feeds v_dot2c the wrong register when it is given a bit-cast element
+    // of a vector instead.
+    auto exp_pair = [&](int pp, float mu, float rs) -> float {
+        const int c4 = pp / 4, j = pp % 4;
+        const int kb = c4 >> 1, g0 = 2 * (c4 & 1);
+        const float p0 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j], c, -mu));
+        const float p1 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j + 1], c, -mu));
+        const bf16x2_t pv2 = {(__bf16)p0, (__bf16)p1};
+        pw[pp] = __builtin_bit_cast(unsigned, pv2);
+        return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
+    };
+
+    // One KV tile of the pipeline, general case.  has_pv: a previous tile's
+    // P V is pending; has_next: the next tile's S is computed here; mask: some
+    // key of this tile is past the sequence end or above this wave's causal
+    // diagonal.
+    auto tile = [&](int t, bool has_pv, bool has_next, bool mask) {
+        const int key0 = t * BN;
+        if (has_pv) pv(sV[(t - 1) & 1], pprev);
+        if (mask) {
+            // key = key0 + 4h + off with off = kb*32 + 8*(r/4) + r%4 a constant;
+            // masked when key >= Sk or (causal) key > qrow
+            int lim = Sk - key0 - 4 * h;
+            if (CAUSAL) lim = min(lim, qrow + 1 - key0 - 4 * h);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = kNegInf;
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, xor32(mx));
+        const float mn = fmaxf(m, mx * c);
+        const float mu = guard_max(mn);
+        const float alpha = exp2_hw(m - mu);
+        float rs = 0.0f;
+#pragma unroll
+        for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+        l = fmaf(l, alpha, rs);
+        m = mn;
+        if (has_next) compute_s(sK[(t + 1) & 1], sacc);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+        for (int c4 = 0; c4 < NC4; ++c4)
+            pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
+    };
+
+    // The hot tile (P V pending, next S due, no mask), with its matrix and
+    // vector work interleaved by hand: each slice between two scheduling
+    // barriers holds one MFMA, the LDS reads of the operand two MFMAs ahead,
+    // and a share of the vector work, so a wave keeps its matrix core busy
+    // while it computes.  Region 1 pairs O += V(t-1)^T P(t-1) with the row
+    // maximum (first four slices) and the exponentials of tile t; region 2
+    // pairs S(t+1) = K(t+1) Q^T with O *= alpha(t).
+    auto hot_tile = [&](int t) {
+        const char* vt8 = reinterpret_cast<const char*>(sV[(t - 1) & 1]);
+        const char* kt8 = reinterpret_cast<const char*>(sK[(t + 1) & 1]);
+        constexpr int NPV = NDB * NC4;  // 16
+        constexpr int NS = NKB * NQC;   // 16
+        constexpr int EPS = NKB * 16 / 4;  // elements per max slice
+        bf16x8_t op[3];
+        op[0] = vread(vt8, 0);
+        op[1] = vread(vt8, 1);
+        float mp[4], mu = 0.0f, mn = 0.0f, alpha = 1.0f, rs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            if (i + 2 < NPV) op[(i + 2) % 3] = vread(vt8, i + 2);
+            oacc[i / NC4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pprev[i % NC4], oacc[i / NC4], 0, 0, 0);
+            if (i < 4) {
+                float x = kNegInf;
+#pragma unroll
+                for (int e = i * EPS; e < (i + 1) * EPS; ++e) x = fmaxf(x, sacc[e / 16][e % 16]);
+                mp[i] = x;
+            }
+            if (i == 3) {
+                float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+                mx = fmaxf(mx, xor32(mx));
+                mn = fmaxf(m, mx * c);
+                mu = guard_max(mn);
+                alpha = exp2_hw(m - mu);
+            }
+            if (i >= 4) {
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (4 + (pp * (NPV - 4)) / NPAIR == i) rs = exp_pair(pp, mu, rs);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l = fmaf(l, alpha, rs);
+        m = mn;
+        op[0] = kread(kt8, 0);
+        op[1] = kread(kt8, 1);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i + 2 < NS) op[(i + 2) % 3] = kread(kt8, i + 2);
+            const int kb = i / NQC, cc = i % NQC;
+            if (cc == 0) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-                for (int cc = 0; cc < NQC; ++cc) {
-                    const bf16x8_t a =
-                        *reinterpret_cast<const bf16x8_t*>(&sK[cur][(kb * 32 + lq) * KST + 16 * cc + 8 * h]);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[cc], sacc[kb], 0, 0, 0);
-                }
             }
-
-            // ---- mask: sequence tail and the causal diagonal --------------
-            if ((key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32)) {
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop[cc], sacc[kb], 0, 0, 0);
+            constexpr int MPS = NDB * 16 / NS;  // rescale multiplies per slice
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= Sk || (CAUSAL && key > qrow)) sacc[kb][r] = kNegInf;
-                    }
-            }
-
-            // ---- online update (base two, scale folded into c) -------------
-            float mx = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, xor32(mx));
-            const float mn = fmaxf(m, mx * c);
-            const float mu = guard_max(mn);
-            const float alpha = exp2_hw(m - mu);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = exp2_hw(fmaf(sacc[kb][r], c, -mu));
-            // The correction is exactly 1 for rows whose maximum did not rise;
-            // when that holds for the whole wave the rescale is skipped (the
-            // conditional form of "Online Softmax" (metalworking),
-            // Recognition guide), which changes no bit of the result.
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            }
-
-            // ---- P to bf16; l sums the same rounded P that multiplies V ----
-            bf16x8_t pop[NC4];
-            float rs = 0.0f;
-            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int c4 = 0; c4 < NC4; ++c4) {
-                const int kb = c4 >> 1, g0 = 2 * (c4 & 1);
-                u32x4_t t4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    // The dot2 operand is the freshly rounded pair itself: hipcc
-                    // (ROCm 7.2) feeds v_dot2c the wrong register when it is
-                    // given a bit-cast element of t4 instead.
-                    const bf16x2_t pv = {(__bf16)sacc[kb][4 * g0 + 2 * j], (__bf16)sacc[kb][4 * g0 + 2 * j + 1]};
-                    t4[j] = __builtin_bit_cast(unsigned, pv);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pv, ones, rs, false);
-                }
-                pop[c4] = __builtin_bit_cast(bf16x8_t, t4);
-            }
-            l = fmaf(l, alpha, rs);
-            m = mn;
-
-            // ---- O^T += V^T P^T -------------------------------------------
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c4 = 0; c4 < NC4; ++c4) {
-                    const bf16x8_t a =
-                        *reinterpret_cast<const bf16x8_t*>(&sV[cur][(db * 32 + lq) * VST + 16 * c4 + 8 * h]);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[c4], oacc[db], 0, 0, 0);
-                }
+            for (int e = i * MPS; e < (i + 1) * MPS; ++e) oacc[e / 16][e % 16] *= alpha;
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (t + 1 < ntiles) lds_store(cur ^ 1);  // buffer cur ^ 1 was last read before the previous barrier
-        if (t + 2 < ntiles) gload(t + 2);
+#pragma unroll
+        for (int c4 = 0; c4 < NC4; ++c4)
+            pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
+    };
+
+    if (ntiles > 0) {
+        dma(kp, sK[0], false, 0);
+        if (ntiles > 1) dma(kp, sK[1], false, BN);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (ntiles > 0) compute_s(sK[0], sacc);
+    __syncthreads();  // every wave has read K(0) before iteration 0 overwrites its buffer with K(2)
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int key0 = t * BN;
+        // buffers t & 1 held V(t-2) and K(t), both read before the last barrier
+        dma(vp, sV[t & 1], true, key0);
+        if (t + 2 < ntiles) dma(kp, sK[t & 1], false, key0 + 2 * BN);
+
+        const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
+        const bool has_pv = t > 0, has_next = t + 1 < ntiles;
+        if (has_pv && has_next && !mask)
+            hot_tile(t);
+        else
+            tile(t, has_pv, has_next, mask);
+        wait_vmem();
         __syncthreads();
     }
+    if (ntiles > 0) pv(sV[(ntiles - 1) & 1], pprev);
 
     // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
     const float lt = l + xor32(l);
@@ -282,20 +399,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     }
 }
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN>
 hipError_t launch_d(const AttnArgs& a)
 {
     const int nqb = (a.Sq + kBM - 1) / kBM;
     const int64_t grid = (int64_t)nqb * a.H * a.B;
     const float c = a.scale * kLog2eHi;
     if (a.out_bf16)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, CAUSAL, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
-                           nqb);
+                           nqb, a.causal ? 1 : 0);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, CAUSAL, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
-                           nqb);
+                           nqb, a.causal ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -304,8 +421,8 @@ hipError_t launch_d(const AttnArgs& a)
 hipError_t launch_attn_fwd(const AttnArgs& a)
 {
     if ((int64_t)a.B * a.H * a.Sq == 0) return hipSuccess;
-    if (a.D == 128) return a.causal ? launch_d<128, 64, true>(a) : launch_d<128, 64, false>(a);
-    return a.causal ? launch_d<64, 128, true>(a) : launch_d<64, 128, false>(a);
+    if (a.D == 128) return launch_d<128, 64>(a);
+    return launch_d<64, 64>(a);
 }
 
 }  // namespace tea
