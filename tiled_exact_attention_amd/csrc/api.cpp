@@ -72,7 +72,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
     if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
     if (causal && Sq != Sk) return TEA_EUNSUPPORTED;
     if ((int64_t)B * H * Sq == 0) return TEA_OK;
-    if ((int64_t)B * H * ((Sq + 127) / 128) > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H * ((Sq + 255) / 256) > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
     if (!q || !o || (Sk > 0 && (!k || !v))) return TEA_EINVAL;
     if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return TEA_EINVAL;
     if (lse_out && !aligned(lse_out, 4)) return TEA_EINVAL;

@@ -4,8 +4,8 @@
 // (curionode), One pass, exactly: blocks stream through fast memory and no
 // row of scores is ever stored).
 //
-// Workgroup: 4 waves, 128 queries (32 per wave); KV tiles of 64 keys
-// double-buffered in LDS.  Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
+// Workgroup: 8 waves, 256 queries (32 per wave), so each K/V tile staged in
+// LDS serves 256 queries; KV tiles of 64 keys, double-buffered.  Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
 //     S^T = K Q^T   (A = K tile from LDS, B = Q^T held in registers)
 //     O^T = V^T P^T (A = V^T tile from LDS, B = P^T straight from the S^T
 //                    accumulators)
@@ -31,7 +31,6 @@ namespace tea {
 
 namespace {
 
-constexpr int kBM = 128;  // queries per workgroup (4 waves x 32)
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -64,6 +63,20 @@ __device__ __forceinline__ int v_swz(int row)
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// One wave-wide 16-byte-per-lane load from HBM straight into LDS: lane i's
+// 16 bytes from `src` land at LDS byte address `dst` + 16 i (dst must be the
+// same in every lane).  Issued as inline assembly so that the compiler does
+// not treat every later LDS read as a possible reader of this write and wait
+// for the load right away (it cannot tell the buffers apart); the kernel
+// instead waits for all such loads (wait_vmem) before the barrier that hands
+// the buffer to its readers.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
+{
+    const unsigned lds = (unsigned)(uintptr_t)dst;  // low 32 bits of a flat LDS address: the LDS offset
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
 // D: head dimension; BN: keys per KV tile.  Two waves per SIMD.
 //
 // Software pipeline: K runs one tile ahead of V.  Iteration t issues the HBM
@@ -74,8 +87,8 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // unconditional (multiplying by exactly 1 where a row's maximum did not rise),
 // which the pages show as the MLX form ("Online Softmax" (metalworking),
 // Recognition guide); it runs under the S MFMAs.
-template <int D, int BN, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+template <int D, int BN, int NW, bool OUT_BF16>
+__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, void* __restrict__ o,
                                                           float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal)
@@ -86,12 +99,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     constexpr int TILE = BN * D;                  // elements per K or V tile (16 KiB)
     constexpr int NCH = D / 8;                    // 16-byte chunks per row
     constexpr int RPI = 1024 / (2 * D);           // rows one wave-wide 16-byte-per-lane load fills
-    constexpr int DPW = TILE * 2 / 1024 / 4;      // such loads per wave per tile
+    constexpr int kBM = 32 * NW;                  // queries per workgroup
+    constexpr int DPW = TILE * 2 / 1024 / NW;     // such loads per wave per tile
     constexpr int NKB = BN / 32;                  // 32-key blocks of S^T
     constexpr int NC4 = BN / 16;                  // 16-key chunks of P^T
     constexpr int NDB = D / 32;                   // 32-wide dimension blocks of O^T
     constexpr int NQC = D / 16;                   // 16-wide contraction chunks of Q K^T
-    static_assert(DPW * 4 * RPI == BN, "tile rows must split evenly over the waves");
+    static_assert(DPW * NW * RPI == BN, "tile rows must split evenly over the waves");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
 
@@ -151,8 +165,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
             // rows past the sequence end repeat the last valid row (its scores
             // are masked, its values meet P = 0)
             const int srow = row < nvalid ? row : nvalid - 1;
-            __builtin_amdgcn_global_load_lds((gptr_t)(g + srow * 2 * D + (chunk << 4)),
-                                             (lptr_t)(tile + (w * DPW + j) * 512), 16, 0, 0);
+            lds_dma16(g + srow * 2 * D + (chunk << 4), tile + (w * DPW + j) * 512);
         }
     };
 
@@ -399,18 +412,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(const uint16_t* __rest
     }
 }
 
-template <int D, int BN>
+template <int D, int BN, int NW>
 hipError_t launch_d(const AttnArgs& a)
 {
-    const int nqb = (a.Sq + kBM - 1) / kBM;
+    constexpr int BM = 32 * NW;
+    const int nqb = (a.Sq + BM - 1) / BM;
     const int64_t grid = (int64_t)nqb * a.H * a.B;
     const float c = a.scale * kLog2eHi;
     if (a.out_bf16)
-        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, true>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, NW, true>), dim3((unsigned)grid), dim3(64 * NW), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
                            nqb, a.causal ? 1 : 0);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, false>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+        hipLaunchKernelGGL((attn_fwd_kernel<D, BN, NW, false>), dim3((unsigned)grid), dim3(64 * NW), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
                            nqb, a.causal ? 1 : 0);
     return hipGetLastError();
@@ -421,8 +435,8 @@ hipError_t launch_d(const AttnArgs& a)
 hipError_t launch_attn_fwd(const AttnArgs& a)
 {
     if ((int64_t)a.B * a.H * a.Sq == 0) return hipSuccess;
-    if (a.D == 128) return launch_d<128, 64>(a);
-    return launch_d<64, 64>(a);
+    if (a.D == 128) return launch_d<128, 64, 8>(a);
+    return launch_d<64, 64, 8>(a);
 }
 
 }  // namespace tea
