@@ -180,15 +180,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     auto compute_s = [&](const uint16_t* kt, f32x16_t* sacc) {
         const char* kb8 = reinterpret_cast<const char*>(kt);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-            for (int cc = 0; cc < NQC; ++cc) {
+        for (int cc = 0; cc < NQC; ++cc)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
                 const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb8 + kro[cc] + kb * 32 * D * 2);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[cc], sacc[kb], 0, 0, 0);
             }
-        }
     };
     // V^T operand via ds_read_b64_tr_b16: in each 16-lane group g, lane
     // s = a + 4 kk points at row 16 c4 + 8 r + 4 h + kk, dims
@@ -218,22 +219,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     auto pv = [&](const uint16_t* vt, const bf16x8_t* pop) {
         const char* vt8 = reinterpret_cast<const char*>(vt);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int c4 = 0; c4 < NC4; ++c4)
 #pragma unroll
-            for (int c4 = 0; c4 < NC4; ++c4) pv_one(vt8, pop, db, c4);
+            for (int db = 0; db < NDB; ++db) pv_one(vt8, pop, db, c4);
     };
 
-    // operand of the i-th PV MFMA (db = i / NC4, c4 = i % NC4) and of the
-    // i-th QK MFMA (kb = i / NQC, cc = i % NQC)
+    // operand of the i-th PV MFMA (db = i % NDB, c4 = i / NDB) and of the
+    // i-th QK MFMA (kb = i % NKB, cc = i / NKB): consecutive MFMAs go to
+    // different accumulators, since a chain of dependent MFMAs issues at
+    // about two thirds of the rate of independent ones
     auto vread = [&](const char* vt8, int i) -> bf16x8_t {
-        const int db = i / NC4, c4 = i % NC4;
+        const int db = i % NDB, c4 = i / NDB;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + 16 * c4 * D * 2));
         const s16x4_t hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + (16 * c4 + 8) * D * 2));
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto kread = [&](const char* kt8, int i) -> bf16x8_t {
-        const int kb = i / NQC, cc = i % NQC;
+        const int kb = i % NKB, cc = i / NKB;
         return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[cc] + kb * 32 * D * 2);
     };
 
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             if (i + 2 < NPV) op[(i + 2) % 3] = vread(vt8, i + 2);
-            oacc[i / NC4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pprev[i % NC4], oacc[i / NC4], 0, 0, 0);
+            oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pprev[i / NDB], oacc[i % NDB], 0, 0, 0);
             if (i < 4) {
                 float x = kNegInf;
 #pragma unroll
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (i + 2 < NS) op[(i + 2) % 3] = kread(kt8, i + 2);
-            const int kb = i / NQC, cc = i % NQC;
+            const int kb = i % NKB, cc = i / NKB;
             if (cc == 0) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
