@@ -304,17 +304,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 
     // The hot tile (P V pending, next S due, no mask), with its matrix and
     // vector work interleaved by hand: each slice between two scheduling
-    // barriers holds one MFMA, the LDS reads of the operand two MFMAs ahead,
+    // barriers holds one MFMA, the LDS reads of an operand two MFMAs ahead,
     // and a share of the vector work, so a wave keeps its matrix core busy
-    // while it computes.  Region 1 pairs O += V(t-1)^T P(t-1) with the row
-    // maximum (first four slices) and the exponentials of tile t; region 2
-    // pairs S(t+1) = K(t+1) Q^T with O *= alpha(t).
+    // while it computes.  The exponentials are split between the two regions
+    // to balance them:
+    //   region 1: O += V(t-1)^T P(t-1) | row maximum, P of keys 0..31
+    //   region 2: S(t+1) keys 0..31    | P of keys 32..63 (still in sacc[1])
+    //             S(t+1) keys 32..63   | O *= alpha(t)
     auto hot_tile = [&](int t) {
+        static_assert(NKB == 2, "the split assumes two 32-key blocks per tile");
         const char* vt8 = reinterpret_cast<const char*>(sV[(t - 1) & 1]);
         const char* kt8 = reinterpret_cast<const char*>(sK[(t + 1) & 1]);
-        constexpr int NPV = NDB * NC4;  // 16
-        constexpr int NS = NKB * NQC;   // 16
+        constexpr int NPV = NDB * NC4;  // MFMAs of region 1
+        constexpr int NS = NKB * NQC;   // MFMAs of region 2
         constexpr int EPS = NKB * 16 / 4;  // elements per max slice
+        constexpr int HP = NPAIR / 2;      // pairs per 32-key block
         bf16x8_t op[3];
         op[0] = vread(vt8, 0);
         op[1] = vread(vt8, 1);
@@ -338,29 +342,39 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
             }
             if (i >= 4) {
 #pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp)
-                    if (4 + (pp * (NPV - 4)) / NPAIR == i) rs = exp_pair(pp, mu, rs);
+                for (int pp = 0; pp < HP; ++pp)
+                    if (4 + (pp * (NPV - 4)) / HP == i) rs = exp_pair(pp, mu, rs);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        l = fmaf(l, alpha, rs);
-        m = mn;
-        op[0] = kread(kt8, 0);
-        op[1] = kread(kt8, 1);
+        // region 2, S MFMAs in key-block order: kb = i / NQC, cc = i % NQC
+        auto kread2 = [&](int i) -> bf16x8_t {
+            return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[i % NQC] + (i / NQC) * 32 * D * 2);
+        };
+        op[0] = kread2(0);
+        op[1] = kread2(1);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            if (i + 2 < NS) op[(i + 2) % 3] = kread(kt8, i + 2);
-            const int kb = i % NKB, cc = i / NKB;
+            if (i + 2 < NS) op[(i + 2) % 3] = kread2(i + 2);
+            const int kb = i / NQC, cc = i % NQC;
             if (cc == 0) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
             }
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop[cc], sacc[kb], 0, 0, 0);
-            constexpr int MPS = NDB * 16 / NS;  // rescale multiplies per slice
+            if (i < NQC) {  // first block's MFMAs: P of the second block of tile t
 #pragma unroll
-            for (int e = i * MPS; e < (i + 1) * MPS; ++e) oacc[e / 16][e % 16] *= alpha;
+                for (int pp = HP; pp < NPAIR; ++pp)
+                    if ((pp - HP) * NQC / HP == i) rs = exp_pair(pp, mu, rs);
+            } else {        // second block's MFMAs: the rescale of O
+                constexpr int MPS = NDB * 16 / NQC;
+#pragma unroll
+                for (int e = (i - NQC) * MPS; e < (i - NQC + 1) * MPS; ++e) oacc[e / 16][e % 16] *= alpha;
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+        l = fmaf(l, alpha, rs);
+        m = mn;
 #pragma unroll
         for (int c4 = 0; c4 < NC4; ++c4)
             pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
