@@ -319,13 +319,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         constexpr int NS = NKB * NQC;   // MFMAs of region 2
         constexpr int EPS = NKB * 16 / 4;  // elements per max slice
         constexpr int HP = NPAIR / 2;      // pairs per 32-key block
+        // region 2 reads its K operands in key-block order (kb = i / NQC, cc = i % NQC)
+        auto kread2 = [&](int i) -> bf16x8_t {
+            return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[i % NQC] + (i / NQC) * 32 * D * 2);
+        };
+        // one ring of three operand registers runs through both regions: slot
+        // (j % 3) holds the operand of the j-th MFMA of the tile (PV first,
+        // then QK), read two MFMAs ahead, so region 2's first K operands are
+        // already in flight during region 1's last MFMAs
         bf16x8_t op[3];
         op[0] = vread(vt8, 0);
         op[1] = vread(vt8, 1);
         float mp[4], mu = 0.0f, mn = 0.0f, alpha = 1.0f, rs = 0.0f;
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
-            if (i + 2 < NPV) op[(i + 2) % 3] = vread(vt8, i + 2);
+            if (i + 2 < NPV)
+                op[(i + 2) % 3] = vread(vt8, i + 2);
+            else
+                op[(i + 2) % 3] = kread2(i + 2 - NPV);
             oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pprev[i / NDB], oacc[i % NDB], 0, 0, 0);
             if (i < 4) {
                 float x = kNegInf;
@@ -347,21 +358,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // region 2, S MFMAs in key-block order: kb = i / NQC, cc = i % NQC
-        auto kread2 = [&](int i) -> bf16x8_t {
-            return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[i % NQC] + (i / NQC) * 32 * D * 2);
-        };
-        op[0] = kread2(0);
-        op[1] = kread2(1);
+        // region 2: S(t+1) MFMAs in key-block order
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            if (i + 2 < NS) op[(i + 2) % 3] = kread2(i + 2);
+            if (i + 2 < NS) op[(NPV + i + 2) % 3] = kread2(i + 2);
             const int kb = i / NQC, cc = i % NQC;
             if (cc == 0) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
             }
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qop[cc], sacc[kb], 0, 0, 0);
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[(NPV + i) % 3], qop[cc], sacc[kb], 0, 0, 0);
             if (i < NQC) {  // first block's MFMAs: P of the second block of tile t
 #pragma unroll
                 for (int pp = HP; pp < NPAIR; ++pp)
