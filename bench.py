@@ -14,7 +14,8 @@ its own roofline fraction.  Each stage is timed with HIP events recorded on
 the stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-Prints one JSON line.
+Warm-up runs at least W steps and at least 0.5 s (--min-warmup-s) so the
+clocks settle; then exactly K steps are timed.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -131,8 +132,10 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="keep warming up until this much wall time has passed (at least --warmup steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode")
@@ -235,10 +238,16 @@ def main():
             if events is not None:
                 events[n][1].record(stream)
 
-    for _ in range(args.warmup):
+    # Warm-up: at least W steps and at least --min-warmup-s seconds of GPU
+    # work, so the engine clock has settled before the timed steps (a cold
+    # MI355X runs its first ~10 ms of MFMA work measurably slower).
+    nwarm = 0
+    w0 = time.perf_counter()
+    while nwarm < args.warmup or time.perf_counter() - w0 < args.min_warmup_s:
         step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
+        torch.cuda.synchronize()
+        nwarm += 1
+    log(f"warmup {nwarm} steps done ({time.perf_counter() - w0:.2f}s)")
 
     evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
            for _ in range(args.steps)]
@@ -279,6 +288,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": nwarm,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -5,15 +5,15 @@
 // Recognition guide: split-KV decode kernels merge partials with the same
 // correction, with no float atomics).
 //
-// Launch 1 (this file): one workgroup per (b, h, chunk).  Chunk c of a
-// sequence of L keys covers keys [floor(c L / S), floor((c+1) L / S)), so
-// chunks are empty when L < S.  Each lane group of D/8 lanes owns one key slot
-// and a slice of 8 dimensions; per step a slot takes U keys, computes their
-// scores (DPP reduction across the group), and folds them into its running
-// (m, l, O) with the online recurrence.  The slots' states are merged inside
-// the wave, the four waves' states through LDS, and the chunk's state is
-// written to the workspace (maxima in base-two units, O unnormalised).
-// K and V are read from HBM exactly once.
+// Launch 1 (this file): one wave per (b, h, chunk).  Chunk c of a sequence of
+// L keys covers keys [floor(c L / S), floor((c+1) L / S)), so chunks are empty
+// when L < S.  Each lane group of D/8 lanes owns one key slot and a slice of 8
+// dimensions; per step a slot takes U keys, computes their scores (DPP
+// reduction across the group), and folds them into its running (m, l, O) with
+// the online recurrence.  The slots' states are merged inside the wave by a
+// butterfly and the chunk's state is written to the workspace (maxima in
+// base-two units, O unnormalised).  K and V are read from HBM exactly once,
+// with non-temporal loads.
 // Launch 2 (merge.hip): a tree merge of the num_splits partials per (b, h).
 #include "common.hpp"
 #include "launch.hpp"
@@ -23,8 +23,6 @@ namespace tea {
 hipError_t launch_merge_base2(const MergeArgs& a);
 
 namespace {
-
-constexpr int kWaves = 4;
 
 template <int D>
 __device__ __forceinline__ float group_sum(float v)
@@ -49,21 +47,24 @@ __device__ __forceinline__ void combine8(float& m1, float& l1, float* O1, float 
     m1 = m;
 }
 
+// One wave per (b, h, chunk): a wave streams its chunk's keys on its own, so
+// there is no LDS and no barrier, and many chunks are in flight per CU.
 template <int D, int U>
 __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ q,
                                                              const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v,
-                                                             const int32_t* __restrict__ kv_len, int H, int Lmax,
-                                                             int S, float scale_log2, float* __restrict__ ws_m,
+                                                             const int32_t* __restrict__ kv_len, int64_t nchunks, int H,
+                                                             int Lmax, int S, float scale_log2, float* __restrict__ ws_m,
                                                              float* __restrict__ ws_l, float* __restrict__ ws_O)
 {
-    constexpr int LPK = D / 8;       // lanes per key
-    constexpr int KPW = 64 / LPK;    // key slots per wave
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int LPK = D / 8;     // lanes per key
+    constexpr int KPW = 64 / LPK;  // key slots per wave
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk handled by this wave
+    if (gw >= nchunks) return;  // whole wave
     const int slot = lane / LPK, dl = lane % LPK;
-    const int64_t bid = blockIdx.x;
-    const int c = (int)(bid % S);
-    const int64_t bh = bid / S;
+    const int c = (int)(gw % S);
+    const int64_t bh = gw / S;
     const int b = (int)(bh / H);
     int L = kv_len[b];
     L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -79,15 +80,16 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
             qs[2 * j + 1] = bf16_hi(w4[j]) * scale_log2;
         }
     }
-    const uint16_t* kb = k + bh * (int64_t)Lmax * D + dl * 8;
-    const uint16_t* vb = v + bh * (int64_t)Lmax * D + dl * 8;
+    const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k + bh * (int64_t)Lmax * D + dl * 8);
+    const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v + bh * (int64_t)Lmax * D + dl * 8);
+    constexpr int RS = D / 8;  // row stride in 16-byte units
 
     float m = kNegInf, l = 0.0f, O[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) O[d] = 0.0f;
 
-    constexpr int STEP = kWaves * U * KPW;  // keys per workgroup step
-    for (int64_t base = k0 + (int64_t)w * U * KPW; base < k1; base += STEP) {
+    // each step: U keys per slot, KPW slots -> U * KPW consecutive keys
+    for (int64_t base = k0; base < k1; base += U * KPW) {
         u32x4_t kr[U], vr[U];
         bool ok[U];
 #pragma unroll
@@ -95,8 +97,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
             int64_t key = base + u * KPW + slot;
             ok[u] = key < k1;
             key = ok[u] ? key : k1 - 1;  // in bounds; its score is masked below
-            kr[u] = *reinterpret_cast<const u32x4_t*>(kb + key * D);
-            vr[u] = *reinterpret_cast<const u32x4_t*>(vb + key * D);
+            kr[u] = __builtin_nontemporal_load(kb + key * RS);
+            vr[u] = __builtin_nontemporal_load(vb + key * RS);
         }
         float s[U];
 #pragma unroll
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
         m = mn;
     }
 
-    // merge the key slots of this wave (butterfly over lane groups)
+    // merge the key slots of this wave (butterfly over lane groups; both
+    // partners combine (lower slot, upper slot) in that order)
 #pragma unroll
     for (int x = LPK; x < 64; x <<= 1) {
         float mp = __shfl_xor(m, x), lp = __shfl_xor(l, x), Op[8];
@@ -153,38 +156,15 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
             combine8(m, l, O, mp, lp, Op);
         }
     }
-
-    // merge the four waves: a balanced tree ((w0, w1), (w2, w3))
-    __shared__ float sm[kWaves], sl[kWaves], sO[kWaves][D];
     if (lane < LPK) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) sO[w][dl * 8 + d] = O[d];
+        const int64_t p = gw;  // = bh * S + c
         if (lane == 0) {
-            sm[w] = m;
-            sl[w] = l;
-        }
-    }
-    __syncthreads();
-    if (w == 0 && lane < LPK) {
-        float m0 = sm[0], l0 = sl[0], m2 = sm[2], l2 = sl[2], O0[8], O1[8], O2[8], O3[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            O0[d] = sO[0][dl * 8 + d];
-            O1[d] = sO[1][dl * 8 + d];
-            O2[d] = sO[2][dl * 8 + d];
-            O3[d] = sO[3][dl * 8 + d];
-        }
-        combine8(m0, l0, O0, sm[1], sl[1], O1);
-        combine8(m2, l2, O2, sm[3], sl[3], O3);
-        combine8(m0, l0, O0, m2, l2, O2);
-        const int64_t p = bh * S + c;
-        if (lane == 0) {
-            ws_m[p] = m0;
-            ws_l[p] = l0;
+            ws_m[p] = m;
+            ws_l[p] = l;
         }
         f32x4v_t* dst = reinterpret_cast<f32x4v_t*>(ws_O + p * D + dl * 8);
-        dst[0] = f32x4v_t{O0[0], O0[1], O0[2], O0[3]};
-        dst[1] = f32x4v_t{O0[4], O0[5], O0[6], O0[7]};
+        dst[0] = f32x4v_t{O[0], O[1], O[2], O[3]};
+        dst[1] = f32x4v_t{O[4], O[5], O[6], O[7]};
     }
 }
 
@@ -199,16 +179,17 @@ size_t decode_workspace_bytes(int B, int H, int D, int num_splits)
 
 hipError_t launch_decode(const DecodeArgs& a)
 {
-    const int64_t grid = (int64_t)a.B * a.H * a.num_splits;
+    const int64_t nchunks = (int64_t)a.B * a.H * a.num_splits;
+    const int64_t grid = (nchunks + 3) / 4;
     const float scale_log2 = a.scale * kLog2eHi;
     if (a.D == 128)
-        hipLaunchKernelGGL((decode_partial_kernel<128, 4>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, a.H, a.Lmax,
-                           a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
+        hipLaunchKernelGGL((decode_partial_kernel<128, 8>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, nchunks, a.H,
+                           a.Lmax, a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
     else
-        hipLaunchKernelGGL((decode_partial_kernel<64, 4>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, a.H, a.Lmax,
-                           a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
+        hipLaunchKernelGGL((decode_partial_kernel<64, 8>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.kv_len, nchunks, a.H,
+                           a.Lmax, a.num_splits, scale_log2, a.ws_m, a.ws_l, a.ws_O);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     MergeArgs m{a.ws_m, a.ws_l, a.ws_O, (int64_t)a.B * a.H, a.num_splits, a.D, nullptr, nullptr, a.o, a.out_bf16,
