@@ -70,7 +70,7 @@ STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) t
     "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
     "attn_nc": ["attn_fwd_kernel<64, 64, 8, true>"],
     "attn_causal": ["attn_fwd_kernel<128, 64, 8, true>"],
-    "decode": ["decode_partial_kernel<128, 4>", "merge_kernel<true, true, true>"],
+    "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
                 "attn_causal": "attn_fwd", "decode": "decode"}
