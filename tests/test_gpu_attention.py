@@ -21,7 +21,7 @@ import torch
 import oracle
 import tiled_exact_attention_amd as tea
 from tiled_exact_attention_amd import inputs
-from gpu_util import check_attention, say, to_np
+from gpu_util import check_attention, half_ulp_bf16, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,84 @@ def test_closed_forms():
     o, lse, _ = _run(q, k, v, False, scale=30.0)
     O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), 30.0, False)
     check_attention(to_np(o), O, "scale 30")
+
+
+def _ramp_inputs(B, H, Sq, Sk, D, slope, seed):
+    """Scores that drift along the keys: q has a unit first component and
+    key j's first component is slope * j, so the score of key j rises (or,
+    for slope < 0, falls) by about slope * j / sqrt(D) on top of N(0, 0.25)
+    noise.  The running maximum then moves in every tile, by amounts below
+    and above the kernel's lag threshold."""
+    q, k, v = inputs.qkv(B, H, Sq, Sk, D, seed=seed)
+    q = (q.float() * 0.5).bfloat16()
+    k = (k.float() * 0.5).bfloat16()
+    q[..., 0] = 1.0
+    k[..., 0] = (slope * torch.arange(Sk, dtype=torch.float32)).bfloat16()
+    return q.contiguous(), k.contiguous(), v
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def _p_rounding_bound(q, k, v, scale, causal, O, L):
+    """Bound on what rounding the weights to bf16 does to O.  With
+    p~_j = p_j (1 + d_j), |d_j| <= 2^-9, and l summed from the same p~, the
+    output is the convex combination sum_j w~_j v_j with
+    w~_j = w_j (1 + d_j) / (1 + sum_i w_i d_i), so
+    |O~ - O| <= 2^-8 / (1 - 2^-9) * sum_j w_j |v_j - O|, per row and dim.
+    The weights w_j = exp(s_j - L) come from the oracle's L (fp64)."""
+    qf, kf, vf = (np.asarray(t, np.float64) for t in (q, k, v))
+    out = np.empty_like(O)
+    Sq, Sk = qf.shape[2], kf.shape[2]
+    for r0 in range(0, Sq, 128):
+        r1 = min(Sq, r0 + 128)
+        s = np.einsum("bhqd,bhkd->bhqk", qf[:, :, r0:r1], kf) * scale
+        if causal:
+            s = np.where(np.arange(Sk)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
+        w = np.exp(s - L[:, :, r0:r1, None])
+        dev = np.abs(vf[:, :, None, :, :] - O[:, :, r0:r1, None, :])  # [b, h, q, k, d]
+        out[:, :, r0:r1] = np.einsum("bhqk,bhqkd->bhqd", w, dev)
+    return out * (2.0 ** -8 / (1.0 - 2.0 ** -9))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("rise", [-8.0, 0.5, 4.0, 12.0, 60.0])
+def test_drifting_maximum(D, causal, rise):
+    """rise: growth of the score per 64-key tile, in base-two units.  Below
+    the kernel's lag (8) its reference trails the running maximum and moves
+    only every few tiles; above it the reference moves every tile; falling
+    scores keep the first tile's maximum.  The result must not depend on
+    which.  With steep rises the weights sit on a few keys, so the 1e-2 of
+    diffuse attention is replaced by the bound the arithmetic gives: the
+    bf16 rounding of the weights (see _p_rounding_bound) plus, for a bf16
+    output, half a bf16 ulp of the result, plus the fp32 summation error."""
+    S = 700
+    slope = rise / 64.0 * math.sqrt(D) / math.log2(math.e)
+    say(f"attn_fwd drifting maximum rise={rise}/tile D={D} causal={causal}")
+    q, k, v = _ramp_inputs(1, 2, S, S, D, slope, seed=int(abs(rise) * 10) + D)
+    o, lse, scale = _run(q, k, v, causal)
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal)
+    # the log-sum-exp also carries the error of the scores themselves: an fp32
+    # dot product of D terms is within D 2^-24 sum_i |q_i k_i| of the exact
+    # one, and the log-sum-exp moves by at most the largest score error
+    qa, ka = np.abs(_np32(q)).astype(np.float64), np.abs(_np32(k)).astype(np.float64)
+    gross = np.einsum("bhqd,bhkd->bhqk", qa, ka)
+    if causal:
+        gross = np.where(np.tril(np.ones((S, S), bool)), gross, 0.0)
+    s_err = D * 2.0 ** -24 * scale * gross.max(axis=-1)
+    assert np.all(np.abs(to_np(lse) - L) <= LSE_TOL + s_err)
+    # fp32 sums of at most S products p v and p, each <= 2^8 |v|max relative
+    # to the reference: S 2^-24 relative error each, on O and on l
+    acc = 2.0 * S * 2.0 ** -24 * float(np.abs(_np32(v)).max())
+    pb = _p_rounding_bound(_np32(q), _np32(k), _np32(v), scale, causal, O, L) + acc
+    err = np.abs(to_np(o).astype(np.float64) - O)
+    lim = half_ulp_bf16(np.abs(O) + pb) + pb  # the ulp of the computed value, which may sit one binade up
+    assert np.all(err <= lim), f"bf16 output: worst err/bound {np.max(err / lim):.3f}"
+    o32, _, _ = _run(q, k, v, causal, out_dtype=torch.float32)
+    err32 = np.abs(to_np(o32).astype(np.float64) - O)
+    assert np.all(err32 <= pb), f"fp32 output: worst err/bound {np.max(err32 / pb):.3f}"
+    print(f"rise {rise}: max abs err bf16 {err.max():.2e}, fp32 {err32.max():.2e}; "
+          f"worst err/bound {np.max(err / lim):.3f} / {np.max(err32 / pb):.3f}")
 
 
 def test_empty_keys_give_zero():

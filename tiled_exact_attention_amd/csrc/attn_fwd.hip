@@ -61,6 +61,9 @@ __device__ __forceinline__ int v_swz(int row)
     else return ((row >> 1) & 1) << 2;
 }
 
+// lag allowed between a row's reference and its running maximum, base two
+constexpr float kLag = 8.0f;
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One wave-wide 16-byte-per-lane load from HBM straight into LDS: lane i's
@@ -81,12 +84,24 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
 //
 // Software pipeline: K runs one tile ahead of V.  Iteration t issues the HBM
 // loads of V(t) and K(t+2), then the MFMAs of O += V(t-1)^T P(t-1) next to the
-// exponentials of tile t, then the MFMAs of S(t+1) = K(t+1) Q^T next to the
-// rescale of O by alpha(t); the two halves of each pair are independent, so
-// the matrix cores and the vector ALUs work at the same time.  The rescale is
-// unconditional (multiplying by exactly 1 where a row's maximum did not rise),
-// which the pages show as the MLX form ("Online Softmax" (metalworking),
-// Recognition guide); it runs under the S MFMAs.
+// row maximum and the first half of the exponentials of tile t, then the MFMAs
+// of S(t+1) = K(t+1) Q^T next to the second half; the two halves of each pair
+// are independent, so the matrix cores and the vector ALUs work at the same
+// time.
+//
+// Lagged reference.  The recurrence subtracts the running maximum so that no
+// exponential overflows ("Online softmax" (roadmapper), The recurrence and
+// Things that break); any reference r with every score - r <= kLag serves as
+// well, since O and l are rescaled together and only their ratio is used.  A
+// row's reference m therefore moves to the tile maximum only when that
+// maximum exceeds m by more than kLag (base two), and O and l are multiplied
+// by 2^(m_old - m_new) only then: every tile with a rise of at most kLag
+// (nearly all tiles after the first) skips the rescale of O, the conditional
+// correction the pages attribute to Metal FlashAttention ("Online Softmax"
+// (metalworking), Recognition guide), taken one step further.  P <= 2^kLag,
+// l <= Sk 2^kLag and O stay far inside fp32 and bf16 range, and rounding is
+// relative, so the result is the same as with the exact running maximum up
+// to rounding.
 template <int D, int BN, int NW, bool OUT_BF16>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
@@ -122,6 +137,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
     const int q0 = qb * kBM;
     const int qrow = q0 + w * 32 + lq;
+    const int qlast = q0 + w * 32 + 31;  // last query of this wave
 
     const uint16_t* qp = q + bh * (int64_t)Sq * D;
     const char* kp = reinterpret_cast<const char*>(k + bh * (int64_t)Sk * D);
@@ -264,9 +280,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     // P V is pending; has_next: the next tile's S is computed here; mask: some
     // key of this tile is past the sequence end or above this wave's causal
     // diagonal.
-    auto tile = [&](int t, bool has_pv, bool has_next, bool mask) {
+    auto tile = [&](int t, auto par, bool has_pv, bool has_next, bool mask) {
+        constexpr int p = decltype(par)::value;  // t & 1
         const int key0 = t * BN;
-        if (has_pv) pv(sV[(t - 1) & 1], pprev);
+        if (has_pv) pv(sV[p ^ 1], pprev);
         if (mask) {
             // key = key0 + 4h + off with off = kb*32 + 8*(r/4) + r%4 a constant;
             // masked when key >= Sk or (causal) key > qrow
@@ -284,15 +301,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         mx = fmaxf(mx, xor32(mx));
-        const float mn = fmaxf(m, mx * c);
+        const float ms = mx * c;
+        const float mn = ms > m + kLag ? ms : m;  // -inf + kLag = -inf: the first finite score moves it
         const float mu = guard_max(mn);
-        const float alpha = exp2_hw(m - mu);
+        const float alpha = exp2_hw(m - mu);     // exactly 1 where the reference stays
         float rs = 0.0f;
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
         l = fmaf(l, alpha, rs);
         m = mn;
-        if (has_next) compute_s(sK[(t + 1) & 1], sacc);
+        if (has_next) compute_s(sK[p ^ 1], sacc);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -310,11 +328,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     // to balance them:
     //   region 1: O += V(t-1)^T P(t-1) | row maximum, P of keys 0..31
     //   region 2: S(t+1) keys 0..31    | P of keys 32..63 (still in sacc[1])
-    //             S(t+1) keys 32..63   | O *= alpha(t)
-    auto hot_tile = [&](int t) {
+    //             S(t+1) keys 32..63   |
+    // then, only when the reference of some row moved, O *= alpha(t).
+    auto hot_tile = [&](int t, auto par) {
+        constexpr int p = decltype(par)::value;  // t & 1
         static_assert(NKB == 2, "the split assumes two 32-key blocks per tile");
-        const char* vt8 = reinterpret_cast<const char*>(sV[(t - 1) & 1]);
-        const char* kt8 = reinterpret_cast<const char*>(sK[(t + 1) & 1]);
+        const char* vt8 = reinterpret_cast<const char*>(sV[p ^ 1]);
+        const char* kt8 = reinterpret_cast<const char*>(sK[p ^ 1]);
         constexpr int NPV = NDB * NC4;  // MFMAs of region 1
         constexpr int NS = NKB * NQC;   // MFMAs of region 2
         constexpr int EPS = NKB * 16 / 4;  // elements per max slice
@@ -331,6 +351,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         op[0] = vread(vt8, 0);
         op[1] = vread(vt8, 1);
         float mp[4], mu = 0.0f, mn = 0.0f, alpha = 1.0f, rs = 0.0f;
+        bool up = false;
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             if (i + 2 < NPV)
@@ -347,7 +368,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
             if (i == 3) {
                 float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
                 mx = fmaxf(mx, xor32(mx));
-                mn = fmaxf(m, mx * c);
+                const float ms = mx * c;
+                up = ms > m + kLag;
+                mn = up ? ms : m;
                 mu = guard_max(mn);
                 alpha = exp2_hw(m - mu);
             }
@@ -372,12 +395,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 #pragma unroll
                 for (int pp = HP; pp < NPAIR; ++pp)
                     if ((pp - HP) * NQC / HP == i) rs = exp_pair(pp, mu, rs);
-            } else {        // second block's MFMAs: the rescale of O
-                constexpr int MPS = NDB * 16 / NQC;
-#pragma unroll
-                for (int e = (i - NQC) * MPS; e < (i - NQC + 1) * MPS; ++e) oacc[e / 16][e % 16] *= alpha;
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // rescale O only if the reference of some row of this wave moved
+        if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
         l = fmaf(l, alpha, rs);
         m = mn;
@@ -395,22 +421,39 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     if (ntiles > 0) compute_s(sK[0], sacc);
     __syncthreads();  // every wave has read K(0) before iteration 0 overwrites its buffer with K(2)
 
-    for (int t = 0; t < ntiles; ++t) {
+    // one iteration per tile; the loop runs two at a time so that the buffer
+    // of each tile (t & 1) is a constant and every LDS address is a per-lane
+    // offset plus an immediate
+    auto step = [&](int t, auto par) {
+        constexpr int p = decltype(par)::value;  // t & 1
         const int key0 = t * BN;
-        // buffers t & 1 held V(t-2) and K(t), both read before the last barrier
-        dma(vp, sV[t & 1], true, key0);
-        if (t + 2 < ntiles) dma(kp, sK[t & 1], false, key0 + 2 * BN);
+        // buffers p held V(t-2) and K(t), both read before the last barrier
+        dma(vp, sV[p], true, key0);
+        if (t + 2 < ntiles) dma(kp, sK[p], false, key0 + 2 * BN);
 
+        // causal: a tile whose first key lies past this wave's last query is
+        // masked for all of the wave's rows (live = false): its P is zero, so
+        // the wave skips it and the P V of it, and computes no S for it; it
+        // still loads its share of every tile and meets every barrier
         const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
-        const bool has_pv = t > 0, has_next = t + 1 < ntiles;
-        if (has_pv && has_next && !mask)
-            hot_tile(t);
-        else
-            tile(t, has_pv, has_next, mask);
+        const bool live = !CAUSAL || key0 <= qlast;
+        const bool has_pv = t > 0 && (!CAUSAL || key0 - BN <= qlast);
+        const bool has_next = t + 1 < ntiles && (!CAUSAL || key0 + BN <= qlast);
+        if (!live) {
+            if (has_pv) pv(sV[p ^ 1], pprev);
+        } else if (has_pv && has_next && !mask) {
+            hot_tile(t, par);
+        } else {
+            tile(t, par, has_pv, has_next, mask);
+        }
         wait_vmem();
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
     }
-    if (ntiles > 0) pv(sV[(ntiles - 1) & 1], pprev);
+    if (ntiles > 0 && (!CAUSAL || (ntiles - 1) * BN <= qlast)) pv(sV[(ntiles - 1) & 1], pprev);
 
     // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
     const float lt = l + xor32(l);
