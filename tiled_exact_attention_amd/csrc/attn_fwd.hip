@@ -82,12 +82,19 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
 
 // D: head dimension; BN: keys per KV tile.  Two waves per SIMD.
 //
-// Software pipeline: K runs one tile ahead of V.  Iteration t issues the HBM
-// loads of V(t) and K(t+2), then the MFMAs of O += V(t-1)^T P(t-1) next to the
-// row maximum and the first half of the exponentials of tile t, then the MFMAs
-// of S(t+1) = K(t+1) Q^T next to the second half; the two halves of each pair
-// are independent, so the matrix cores and the vector ALUs work at the same
-// time.
+// Two groups of four waves per workgroup, one wave of each group on every
+// SIMD, take turns ("ping-pong"): while one group runs the matrix phase of a
+// tile (M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, MFMAs fed from LDS)
+// the other runs the softmax phase (X: row maximum, reference, exponentials,
+// P), which is vector work only.  A SIMD then overlaps one wave's MFMAs with
+// the other wave's vector instructions.  Each wave alternates X(t), M(t),
+// X(t+1), ...; group 1 runs one phase behind group 0, and every phase ends
+// at a workgroup barrier:
+//   slot 2t  : group 0 X(t)        group 1 M(t-1)
+//   slot 2t+1: group 0 M(t)        group 1 X(t)      + loads of V(t+1), K(t+2)
+// M(t) reads V(t) and K(t+1) (slots 2t+1 and 2t+2); the loads issued in slot
+// 2t+1 overwrite V(t-1) and K(t), last read in slot 2t, and are waited for at
+// the end of slot 2t+2, before their first reader.
 //
 // Lagged reference.  The recurrence subtracts the running maximum so that no
 // exponential overflows ("Online softmax" (roadmapper), The recurrence and
@@ -108,6 +115,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
                                                           const uint16_t* __restrict__ v, void* __restrict__ o,
                                                           float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal)
 {
+    static_assert(NW == 8, "two groups of four waves, one wave of each group per SIMD");
     // causal is a runtime flag: as a template parameter it made hipcc spill
     // the non-causal instantiation
     const bool CAUSAL = causal != 0;
@@ -126,12 +134,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lq = lane & 31, h = lane >> 5;
+    const int grp = w >> 2;  // waves w and w + 4 share a SIMD
 
     // Workgroups are dealt to the 8 XCDs round robin; regroup them so the
     // query blocks of one (b, h) run on one XCD and share its L2 copy of K, V.
-    const int T = gridDim.x;
+    const int G = gridDim.x;
     const int bid = blockIdx.x;
-    const int logical = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+    const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
     int qb = logical % nqb;
     const int64_t bh = logical / nqb;
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
@@ -165,6 +174,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 
     const int kend = CAUSAL ? (Sk < q0 + kBM ? Sk : q0 + kBM) : Sk;
     const int ntiles = (kend + BN - 1) / BN;
+    // tiles after tlast hold no key visible to any query of this wave
+    const int tlast = CAUSAL ? min(ntiles - 1, qlast / BN) : ntiles - 1;
 
     // ---- HBM -> LDS: lane `lane` of this wave's j-th load fills 16 bytes
     // at byte (w * DPW + j) * 1024 + 16 * lane of the tile, i.e. row
@@ -193,20 +204,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     int kro[NQC];
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) kro[cc] = (lq * D + (((2 * cc + h) ^ kswz) << 3)) * 2;
-    auto compute_s = [&](const uint16_t* kt, f32x16_t* sacc) {
-        const char* kb8 = reinterpret_cast<const char*>(kt);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-        for (int cc = 0; cc < NQC; ++cc)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb8 + kro[cc] + kb * 32 * D * 2);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[cc], sacc[kb], 0, 0, 0);
-            }
-    };
     // V^T operand via ds_read_b64_tr_b16: in each 16-lane group g, lane
     // s = a + 4 kk points at row 16 c4 + 8 r + 4 h + kk, dims
     // 32 db + 16 (g % 2) + 4 a .. +4; the transposing read then hands lane
@@ -216,34 +213,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     // keeps one byte offset per db and (c4, r) add constants.
     int vro[NDB];
     {
-        const int grp = lane >> 4, sl = lane & 15;
+        const int g16 = lane >> 4, sl = lane & 15;
         const int vk = sl >> 2, va = sl & 3;
         const int vrow0 = 4 * h + vk;
-        const int vchunk = 2 * (grp & 1) + (va >> 1);
+        const int vchunk = 2 * (g16 & 1) + (va >> 1);
         const int vswz = v_swz<D>(vrow0);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             vro[db] = (vrow0 * D + (((4 * db + vchunk) ^ vswz) << 3) + ((va & 1) << 2)) * 2;
     }
-    auto pv_one = [&](const char* vt8, const bf16x8_t* pop, int db, int c4) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + 16 * c4 * D * 2));
-        const s16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + (16 * c4 + 8) * D * 2));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[c4], oacc[db], 0, 0, 0);
-    };
-    auto pv = [&](const uint16_t* vt, const bf16x8_t* pop) {
-        const char* vt8 = reinterpret_cast<const char*>(vt);
-#pragma unroll
-        for (int c4 = 0; c4 < NC4; ++c4)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) pv_one(vt8, pop, db, c4);
-    };
-
-    // operand of the i-th PV MFMA (db = i % NDB, c4 = i / NDB) and of the
-    // i-th QK MFMA (kb = i % NKB, cc = i / NKB): consecutive MFMAs go to
-    // different accumulators, since a chain of dependent MFMAs issues at
-    // about two thirds of the rate of independent ones
+    // A operand of the j-th MFMA of the matrix phase: first the P V MFMAs
+    // (db = j % NDB, c4 = j / NDB), then the Q K MFMAs (kb = i % NKB,
+    // cc = i / NKB with i = j - NPV): consecutive MFMAs go to different
+    // accumulators, since back-to-back dependent MFMAs issue at about two
+    // thirds of the rate of independent ones when one wave has the SIMD's
+    // matrix core to itself
     auto vread = [&](const char* vt8, int i) -> bf16x8_t {
         const int db = i % NDB, c4 = i / NDB;
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_p)(vt8 + vro[db] + 16 * c4 * D * 2));
@@ -276,14 +260,40 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
     };
 
-    // One KV tile of the pipeline, general case.  has_pv: a previous tile's
-    // P V is pending; has_next: the next tile's S is computed here; mask: some
-    // key of this tile is past the sequence end or above this wave's causal
-    // diagonal.
-    auto tile = [&](int t, auto par, bool has_pv, bool has_next, bool mask) {
-        constexpr int p = decltype(par)::value;  // t & 1
+    // ---- matrix phase M(t): O += V(t)^T P(t) (DO_PV), S(t+1) = K(t+1) Q^T
+    // (DO_S).  MFMAs only, with their operands read from LDS through a ring of
+    // R registers, R - 1 MFMAs ahead.
+    constexpr int NPV = NDB * NC4, NS = NKB * NQC;
+    auto mphase = [&](auto pv_c, auto s_c, const char* vt8, const char* kt8) {
+        constexpr bool DO_PV = decltype(pv_c)::value, DO_S = decltype(s_c)::value;
+        constexpr int N0 = DO_PV ? NPV : 0;
+        constexpr int N = N0 + (DO_S ? NS : 0);
+        constexpr int R = 4;
+        auto rd = [&](int j) -> bf16x8_t { return j < N0 ? vread(vt8, j) : kread(kt8, j - N0); };
+        bf16x8_t op[R];
+#pragma unroll
+        for (int j = 0; j < R - 1; ++j)
+            if (j < N) op[j] = rd(j);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            if (j + R - 1 < N) op[(j + R - 1) % R] = rd(j + R - 1);
+            if (j < N0) {
+                oacc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], pprev[j / NDB], oacc[j % NDB], 0, 0, 0);
+            } else {
+                const int i = j - N0, kb = i % NKB, cc = i / NKB;
+                if (cc == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+                }
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], qop[cc], sacc[kb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // ---- softmax phase X(t) on S(t) (in sacc): vector work only ----------
+    auto xphase = [&](int t) {
         const int key0 = t * BN;
-        if (has_pv) pv(sV[p ^ 1], pprev);
+        const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
         if (mask) {
             // key = key0 + 4h + off with off = kb*32 + 8*(r/4) + r%4 a constant;
             // masked when key >= Sk or (causal) key > qrow
@@ -302,102 +312,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         mx = fmaxf(mx, xor32(mx));
         const float ms = mx * c;
-        const float mn = ms > m + kLag ? ms : m;  // -inf + kLag = -inf: the first finite score moves it
+        const bool up = ms > m + kLag;            // -inf + kLag = -inf: the first finite score moves it
+        const float mn = up ? ms : m;
         const float mu = guard_max(mn);
-        const float alpha = exp2_hw(m - mu);     // exactly 1 where the reference stays
+        const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
         float rs = 0.0f;
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
         l = fmaf(l, alpha, rs);
         m = mn;
-        if (has_next) compute_s(sK[p ^ 1], sacc);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-#pragma unroll
-        for (int c4 = 0; c4 < NC4; ++c4)
-            pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
-    };
-
-    // The hot tile (P V pending, next S due, no mask), with its matrix and
-    // vector work interleaved by hand: each slice between two scheduling
-    // barriers holds one MFMA, the LDS reads of an operand two MFMAs ahead,
-    // and a share of the vector work, so a wave keeps its matrix core busy
-    // while it computes.  The exponentials are split between the two regions
-    // to balance them:
-    //   region 1: O += V(t-1)^T P(t-1) | row maximum, P of keys 0..31
-    //   region 2: S(t+1) keys 0..31    | P of keys 32..63 (still in sacc[1])
-    //             S(t+1) keys 32..63   |
-    // then, only when the reference of some row moved, O *= alpha(t).
-    auto hot_tile = [&](int t, auto par) {
-        constexpr int p = decltype(par)::value;  // t & 1
-        static_assert(NKB == 2, "the split assumes two 32-key blocks per tile");
-        const char* vt8 = reinterpret_cast<const char*>(sV[p ^ 1]);
-        const char* kt8 = reinterpret_cast<const char*>(sK[p ^ 1]);
-        constexpr int NPV = NDB * NC4;  // MFMAs of region 1
-        constexpr int NS = NKB * NQC;   // MFMAs of region 2
-        constexpr int EPS = NKB * 16 / 4;  // elements per max slice
-        constexpr int HP = NPAIR / 2;      // pairs per 32-key block
-        // region 2 reads its K operands in key-block order (kb = i / NQC, cc = i % NQC)
-        auto kread2 = [&](int i) -> bf16x8_t {
-            return *reinterpret_cast<const bf16x8_t*>(kt8 + kro[i % NQC] + (i / NQC) * 32 * D * 2);
-        };
-        // one ring of three operand registers runs through both regions: slot
-        // (j % 3) holds the operand of the j-th MFMA of the tile (PV first,
-        // then QK), read two MFMAs ahead, so region 2's first K operands are
-        // already in flight during region 1's last MFMAs
-        bf16x8_t op[3];
-        op[0] = vread(vt8, 0);
-        op[1] = vread(vt8, 1);
-        float mp[4], mu = 0.0f, mn = 0.0f, alpha = 1.0f, rs = 0.0f;
-        bool up = false;
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            if (i + 2 < NPV)
-                op[(i + 2) % 3] = vread(vt8, i + 2);
-            else
-                op[(i + 2) % 3] = kread2(i + 2 - NPV);
-            oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pprev[i / NDB], oacc[i % NDB], 0, 0, 0);
-            if (i < 4) {
-                float x = kNegInf;
-#pragma unroll
-                for (int e = i * EPS; e < (i + 1) * EPS; ++e) x = fmaxf(x, sacc[e / 16][e % 16]);
-                mp[i] = x;
-            }
-            if (i == 3) {
-                float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-                mx = fmaxf(mx, xor32(mx));
-                const float ms = mx * c;
-                up = ms > m + kLag;
-                mn = up ? ms : m;
-                mu = guard_max(mn);
-                alpha = exp2_hw(m - mu);
-            }
-            if (i >= 4) {
-#pragma unroll
-                for (int pp = 0; pp < HP; ++pp)
-                    if (4 + (pp * (NPV - 4)) / HP == i) rs = exp_pair(pp, mu, rs);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // region 2: S(t+1) MFMAs in key-block order
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            if (i + 2 < NS) op[(NPV + i + 2) % 3] = kread2(i + 2);
-            const int kb = i / NQC, cc = i % NQC;
-            if (cc == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-            }
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[(NPV + i) % 3], qop[cc], sacc[kb], 0, 0, 0);
-            if (i < NQC) {  // first block's MFMAs: P of the second block of tile t
-#pragma unroll
-                for (int pp = HP; pp < NPAIR; ++pp)
-                    if ((pp - HP) * NQC / HP == i) rs = exp_pair(pp, mu, rs);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
         // rescale O only if the reference of some row of this wave moved
         if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
@@ -405,55 +328,54 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
-        l = fmaf(l, alpha, rs);
-        m = mn;
 #pragma unroll
         for (int c4 = 0; c4 < NC4; ++c4)
             pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
     };
 
+    // ---- prologue: K(0), V(0), K(1); every wave computes its S(0) ----------
     if (ntiles > 0) {
         dma(kp, sK[0], false, 0);
+        dma(vp, sV[0], true, 0);
         if (ntiles > 1) dma(kp, sK[1], false, BN);
     }
     wait_vmem();
     __syncthreads();
-    if (ntiles > 0) compute_s(sK[0], sacc);
-    __syncthreads();  // every wave has read K(0) before iteration 0 overwrites its buffer with K(2)
+    if (ntiles > 0) mphase(std::false_type{}, std::true_type{}, nullptr, reinterpret_cast<const char*>(sK[0]));
+    if (grp == 1) __syncthreads();  // group 1 runs one slot behind group 0
 
-    // one iteration per tile; the loop runs two at a time so that the buffer
-    // of each tile (t & 1) is a constant and every LDS address is a per-lane
-    // offset plus an immediate
-    auto step = [&](int t, auto par) {
-        constexpr int p = decltype(par)::value;  // t & 1
-        const int key0 = t * BN;
-        // buffers p held V(t-2) and K(t), both read before the last barrier
-        dma(vp, sV[p], true, key0);
-        if (t + 2 < ntiles) dma(kp, sK[p], false, key0 + 2 * BN);
-
-        // causal: a tile whose first key lies past this wave's last query is
-        // masked for all of the wave's rows (live = false): its P is zero, so
-        // the wave skips it and the P V of it, and computes no S for it; it
-        // still loads its share of every tile and meets every barrier
-        const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
-        const bool live = !CAUSAL || key0 <= qlast;
-        const bool has_pv = t > 0 && (!CAUSAL || key0 - BN <= qlast);
-        const bool has_next = t + 1 < ntiles && (!CAUSAL || key0 + BN <= qlast);
-        if (!live) {
-            if (has_pv) pv(sV[p ^ 1], pprev);
-        } else if (has_pv && has_next && !mask) {
-            hot_tile(t, par);
-        } else {
-            tile(t, par, has_pv, has_next, mask);
+    // loads of V(t+1) and K(t+2), issued in slot 2t+1 into the buffers of
+    // V(t-1) and K(t), whose last reader ran in slot 2t
+    auto loads = [&](int t, auto par) {
+        constexpr int P = decltype(par)::value;
+        if (t + 1 < ntiles) dma(vp, sV[P ^ 1], true, (t + 1) * BN);
+        if (t + 2 < ntiles) dma(kp, sK[P], false, (t + 2) * BN);
+    };
+    // X(t) then M(t) for one tile; P = t & 1 is a constant, so every LDS
+    // address is a per-lane offset plus an immediate
+    auto tile = [&](int t, auto par) {
+        constexpr int P = decltype(par)::value;
+        // X(t): slot 2t for group 0, 2t+1 for group 1
+        if (grp == 1) loads(t, par);
+        if (t <= tlast) xphase(t);
+        if (grp == 0) wait_vmem();  // loads issued in slot 2t-1, read from slot 2t+1
+        __syncthreads();
+        // M(t): slot 2t+1 for group 0, 2t+2 for group 1
+        if (grp == 0) loads(t, par);
+        if (t <= tlast) {
+            __builtin_amdgcn_s_setprio(1);  // this wave's MFMAs go ahead of its partner's vector work
+            mphase(std::true_type{}, std::true_type{}, reinterpret_cast<const char*>(sV[P]),
+                   reinterpret_cast<const char*>(sK[P ^ 1]));
+            __builtin_amdgcn_s_setprio(0);
         }
-        wait_vmem();
+        if (grp == 1) wait_vmem();  // loads issued in slot 2t+1, read from slot 2t+3
         __syncthreads();
     };
     for (int t = 0; t < ntiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
     }
-    if (ntiles > 0 && (!CAUSAL || (ntiles - 1) * BN <= qlast)) pv(sV[(ntiles - 1) & 1], pprev);
+    if (grp == 0) __syncthreads();  // the barrier of group 1's extra slot
 
     // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
     const float lt = l + xor32(l);
