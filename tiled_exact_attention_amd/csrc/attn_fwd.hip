@@ -61,8 +61,9 @@ __device__ __forceinline__ int v_swz(int row)
     else return ((row >> 1) & 1) << 2;
 }
 
-// lag allowed between a row's reference and its running maximum, base two
-constexpr float kLag = 8.0f;
+// largest sum of one lane's P for a tile (32 keys) taken against a row's
+// reference before the reference has to move: no single P then exceeds it
+constexpr float kMaxTileSum = 256.0f;
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -98,17 +99,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
 //
 // Lagged reference.  The recurrence subtracts the running maximum so that no
 // exponential overflows ("Online softmax" (roadmapper), The recurrence and
-// Things that break); any reference r with every score - r <= kLag serves as
-// well, since O and l are rescaled together and only their ratio is used.  A
-// row's reference m therefore moves to the tile maximum only when that
-// maximum exceeds m by more than kLag (base two), and O and l are multiplied
-// by 2^(m_old - m_new) only then: every tile with a rise of at most kLag
-// (nearly all tiles after the first) skips the rescale of O, the conditional
-// correction the pages attribute to Metal FlashAttention ("Online Softmax"
-// (metalworking), Recognition guide), taken one step further.  P <= 2^kLag,
-// l <= Sk 2^kLag and O stay far inside fp32 and bf16 range, and rounding is
-// relative, so the result is the same as with the exact running maximum up
-// to rounding.
+// Things that break); any reference r with every score - r small enough
+// serves as well, since O and l are taken relative to the same r and only
+// their ratio is used (and LSE = r + log l).  The softmax phase therefore
+// first takes P against the row's current reference, without the tile
+// maximum; if every lane's sum of P for the tile is at most kMaxTileSum
+// (so no single P exceeds it) that P stands.  Otherwise (and on a row's
+// first tile) the reference moves to the running maximum, O and l are
+// multiplied by 2^(m_old - m_new), and P is taken again: a conditional
+// correction as the pages attribute to Metal FlashAttention ("Online Softmax"
+// (metalworking), Recognition guide), taken one step further.  The
+// reference is always a past running maximum, so some key of the row has
+// P >= 1 and nothing underflows that the exact recurrence keeps; P <= 2^8
+// and l <= Sk 2^8 stay far inside fp32 and bf16 range, and rounding is
+// relative, so the result equals that of the exact running maximum up to
+// rounding.
 template <int D, int BN, int NW, bool OUT_BF16>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         }
     };
     // ---- softmax phase X(t) on S(t) (in sacc): vector work only ----------
-    auto xphase = [&](int t) {
+    auto xphase = [&](int t) __attribute__((always_inline)) {
         const int key0 = t * BN;
         const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
         if (mask) {
@@ -305,29 +310,44 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = kNegInf;
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = fmaxf(mx, xor32(mx));
-        const float ms = mx * c;
-        const bool up = ms > m + kLag;            // -inf + kLag = -inf: the first finite score moves it
-        const float mn = up ? ms : m;
-        const float mu = guard_max(mn);
-        const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
+        // fast path: P against the row's current reference, without the
+        // tile maximum.  It stands when every lane's sum of P is at most
+        // 2^kLag (so no single P exceeds it) and the row has a reference.
         float rs = 0.0f;
+        {
+            const float mu = guard_max(m);
 #pragma unroll
-        for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
-        l = fmaf(l, alpha, rs);
-        m = mn;
-        // rescale O only if the reference of some row of this wave moved
-        if (__builtin_amdgcn_ballot_w64(up)) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
         }
+        const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
+        if (__builtin_amdgcn_ballot_w64(redo)) {
+            // slow path (the first tile of a row, a large rise, or a NaN):
+            // the reference moves to the running maximum, O and l follow it,
+            // and P is taken again against it
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mx = fmaxf(mx, xor32(mx));
+            const float ms = mx * c;
+            const bool up = ms > m;                   // m = -inf: any finite score moves it
+            const float mn = up ? ms : m;
+            const float mu = guard_max(mn);
+            const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
+            rs = 0.0f;
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+            l *= alpha;
+            m = mn;
+            if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+        }
+        l += rs;
 #pragma unroll
         for (int c4 = 0; c4 < NC4; ++c4)
             pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
