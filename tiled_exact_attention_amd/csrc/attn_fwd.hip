@@ -444,7 +444,7 @@ hipError_t launch_attn_fwd(const AttnArgs& a)
 {
     if ((int64_t)a.B * a.H * a.Sq == 0) return hipSuccess;
     if (a.D == 128) return launch_d<128, 64, 8>(a);
-    return launch_d<64, 64, 8>(a);
+    return launch_d<64, 128, 8>(a);
 }
 
 }  // namespace tea
