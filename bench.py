@@ -68,7 +68,7 @@ def measured_traffic(kernel: str, workload: str):
 STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) that make up one launch
     "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256>"],
     "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
-    "attn_nc": ["attn_fwd_kernel<64, 64, 8, true>"],
+    "attn_nc": ["attn_fwd_kernel<64, 128, 8, true>"],
     "attn_causal": ["attn_fwd_kernel<128, 64, 8, true>"],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
 }

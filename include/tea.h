@@ -58,7 +58,11 @@ enum tea_dtype { TEA_F32 = 0, TEA_BF16 = 1 };
  *           4-byte (f32) or 2-byte (bf16) aligned; rows whose start is
  *           16-byte aligned take 128-bit loads.
  *   rows    >= 0 (0: nothing to do).
- *   cols    0 .. 16384 (0: every row is the empty set; larger: TEA_EUNSUPPORTED).
+ *   cols    >= 0 (0: every row is the empty set).  Rows of up to 16384 logits
+ *           are read once and written once; longer rows are streamed twice
+ *           (maximum and normaliser in one read, the output in the second),
+ *           one workgroup per row (the original setting of the online
+ *           normaliser, "The Online Softmax" (curionode), intro).
  *   block   logits folded per online step in each lane: 1, 2, 4, 8, 16, 32,
  *           or 0 for the default 8; values above a lane's share act as one
  *           block per lane; other values: TEA_EUNSUPPORTED.  The result does

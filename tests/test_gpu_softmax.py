@@ -4,7 +4,8 @@ Workloads: 4096 x 1024 fp32 logits N(0,1) x {1, 1000} in blocks of 8 and the
 64-logit vector ("The Online Softmax" (curionode), Workshop and One pass,
 exactly); 65536 x 8192 in fp32 and bf16 at scales {1, 30, 1000}, compared on
 sampled rows and by properties that hold at any size; ragged and tiny row
-lengths, every block size, empty rows and in-place operation.
+lengths, every block size, empty rows and in-place operation; rows longer
+than 16384 (up to a million logits), which take the two-read streaming path.
 """
 import math
 
@@ -107,6 +108,52 @@ def test_in_place_and_empty_and_all_neg_inf():
     assert y0.shape == (5, 0) and torch.all(m0 == -math.inf) and torch.all(l0 == 0)
     z = tea.row_softmax(torch.empty((0, 100), device=DEV))
     assert z.shape == (0, 100)
+
+
+# ---- rows longer than 16384: the streaming two-read path --------------------
+
+@pytest.mark.parametrize("cols", [16385, 16388, 20000, 65536, 100003])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_rows(cols, dtype):
+    """Rows that no longer fit in a workgroup's registers are streamed twice
+    (maximum and normaliser in one read, the output in a second); aligned
+    lengths take 128-bit loads, the others the scalar path."""
+    say(f"row_softmax long rows cols={cols} {dtype}")
+    x = inputs.logits(9, cols, 30.0, 2000 + cols % 997, dtype)
+    y, m, l = _run(x)
+    _compare(x, y, m, l, 1e-5 if dtype == "f32" else 4e-3, f"cols={cols} {dtype}")
+
+
+@pytest.mark.parametrize("block", [1, 2, 4, 8, 16, 32, 64])
+def test_long_rows_block_sizes(block):
+    say(f"row_softmax long rows block={block}")
+    x = inputs.logits(5, 40000, 1000.0, 3000 + block, "f32")
+    y, m, l = _run(x, block=block)
+    _compare(x, y, m, l, 1e-5, f"long rows block={block}")
+
+
+def test_long_rows_special():
+    """A million logits per row at scale 1000, a row of -inf, a row with one
+    finite logit, in place, a misaligned base pointer (scalar path)."""
+    say("row_softmax 4 x 1000000 f32 x1000, -inf rows, in place, misaligned")
+    x_cpu = inputs.logits(4, 1_000_000, 1000.0, 4001, "f32")
+    x_cpu[1] = -math.inf
+    x_cpu[2, :] = -math.inf
+    x_cpu[2, 777_777] = 3.0
+    x = x_cpu.to(DEV)
+    ref, mref, lref = oracle.softmax_rows(x_cpu.numpy())
+    y, m, l = tea.row_softmax(x, out=x, stats=True)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr()
+    check_softmax(to_np(y), ref, 1e-5, "1e6 logits in place")
+    assert np.all(to_np(y)[1] == 0.0) and to_np(m)[1] == -math.inf and to_np(l)[1] == 0.0
+    assert to_np(y)[2, 777_777] == 1.0 and to_np(l)[2] == 1.0
+    xs = torch.empty(3 * 30000 + 1, device=DEV)[1:].view(3, 30000)
+    xm_cpu = inputs.logits(3, 30000, 5.0, 4002, "f32")
+    xs.copy_(xm_cpu)
+    ym, mm, lm = tea.row_softmax(xs, stats=True)
+    torch.cuda.synchronize()
+    _compare(xm_cpu, ym, mm, lm, 1e-5, "long rows misaligned")
 
 
 def test_deterministic():

@@ -187,6 +187,145 @@ __global__ __launch_bounds__(WG) void row_softmax_kernel(const void* xv, void* y
     }
 }
 
+// Rows longer than the registers of a workgroup hold (cols > 16384): the
+// online normaliser as its authors first used it ("The Online Softmax"
+// (curionode), intro: two reads and one write per element instead of the
+// safe softmax's three reads and one write).  One workgroup of WG lanes per
+// row; pass 1 streams the row once, each lane folding UN loads (UN * W
+// logits) per step in blocks of BLOCK with the recurrence above, and the
+// lanes' states are merged as above; pass 2 streams the row again and writes
+// y = exp(x - M) / L.
+template <bool BF16, bool VEC, int BLOCK, int WG>
+__global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, void* yv, int64_t cols,
+                                                                float* __restrict__ m_out, float* __restrict__ l_out)
+{
+    constexpr int W = VEC ? (BF16 ? 8 : 4) : 1;  // elements per load
+    constexpr int UN = VEC ? 4 : 16;              // loads per lane per step
+    constexpr int N = UN * W;                     // logits per lane per step
+    constexpr int B = BLOCK < N ? BLOCK : N;
+    constexpr int NWAVE = WG / 64;
+    static_assert(N % B == 0, "bad block");
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int64_t nvec = cols / W;  // loads in the row (128-bit loads are taken only when W divides cols)
+
+    auto load = [&](int64_t vi, float* x) {
+        if (vi >= nvec) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) x[k] = kNegInf;
+            return;
+        }
+        if constexpr (VEC) {
+            if constexpr (BF16) {
+                const u32x4_t w = *(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(xv) + row * cols) + vi);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    x[2 * k] = bf16_lo(w[k]);
+                    x[2 * k + 1] = bf16_hi(w[k]);
+                }
+            } else {
+                const f32x4v_t w = *(reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(xv) + row * cols) + vi);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x[k] = w[k];
+            }
+        } else {
+            if constexpr (BF16)
+                x[0] = __uint_as_float((unsigned)static_cast<const uint16_t*>(xv)[row * cols + vi] << 16);
+            else
+                x[0] = static_cast<const float*>(xv)[row * cols + vi];
+        }
+    };
+
+    // ---- pass 1: fold -------------------------------------------------------
+    float m = kNegInf, l = 0.0f;
+    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)UN * WG) {
+        float x[N];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) load(v0 + (int64_t)u * WG + t, x + u * W);
+#pragma unroll
+        for (int b0 = 0; b0 < N; b0 += B) {
+            float bm = x[b0];
+#pragma unroll
+            for (int e = 1; e < B; ++e) bm = fmaxf(bm, x[b0 + e]);
+            const float mn = fmaxf(m, bm);
+            const float mu = guard_max(mn);
+            const float c = exp2_hw((m - mu) * kLog2eHi);
+            float s = 0.0f;
+#pragma unroll
+            for (int e = 0; e < B; ++e) s += exp2_hw((x[b0 + e] - mu) * kLog2eHi);
+            l = fmaf(l, c, s);
+            m = mn;
+        }
+    }
+    // ---- merge the lanes' states -------------------------------------------
+    float M = wave_reduce(m, MaxOp());
+    float L = wave_reduce(l * exp2_hw((m - guard_max(M)) * kLog2eHi), AddOp());
+    {
+        __shared__ float sm[NWAVE], sl[NWAVE];
+        const int w = t / 64;
+        if ((t & 63) == 0) {
+            sm[w] = M;
+            sl[w] = L;
+        }
+        __syncthreads();
+        M = sm[0];
+#pragma unroll
+        for (int k = 1; k < NWAVE; ++k) M = fmaxf(M, sm[k]);
+        const float mu = guard_max(M);
+        L = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NWAVE; ++k) L += sl[k] * exp2_hw((sm[k] - mu) * kLog2eHi);
+    }
+    if (t == 0) {
+        if (m_out) m_out[row] = M;
+        if (l_out) l_out[row] = L;
+    }
+
+    // ---- pass 2: normalise and write ---------------------------------------
+    const float mu = guard_max(M);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float mh = mu * kLog2eHi;
+    const float ml = fmaf(mu, kLog2eHi, -mh) + mu * kLog2eLo;  // tail of M*log2(e)
+    for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)UN * WG) {
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int64_t vi = v0 + (int64_t)u * WG + t;
+            if (vi >= nvec) break;
+            float x[W], y[W];
+            load(vi, x);
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                if constexpr (BF16) {
+                    y[k] = exp2_hw((x[k] - mu) * kLog2eHi) * inv;
+                } else {
+                    const float th = fmaf(x[k], kLog2eHi, -mh);
+                    const float tl = fmaxf(fmaf(x[k], kLog2eLo, -ml), -1.0f);
+                    const float p = exp2_hw(th) * inv;
+                    y[k] = fminf(fmaf(p, tl * kLn2, p), 1.0f);
+                }
+            }
+            if constexpr (VEC) {
+                if constexpr (BF16) {
+                    u32x4_t w;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(y[2 * k], y[2 * k + 1]);
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(yv) + row * cols) + vi);
+                } else {
+                    const f32x4v_t w = {y[0], y[1], y[2], y[3]};
+                    __builtin_nontemporal_store(w, reinterpret_cast<f32x4v_t*>(static_cast<float*>(yv) + row * cols) + vi);
+                }
+            } else {
+                if constexpr (BF16) {
+                    bf16x2_t v = {(__bf16)y[0], (__bf16)0.0f};
+                    static_cast<uint16_t*>(yv)[row * cols + vi] = (uint16_t)(__builtin_bit_cast(unsigned, v) & 0xffffu);
+                } else {
+                    static_cast<float*>(yv)[row * cols + vi] = y[0];
+                }
+            }
+        }
+    }
+}
+
 // Empty rows (cols == 0): each is the empty set, (m, l) = (-inf, 0).
 __global__ void empty_rows_kernel(int64_t rows, float* m_out, float* l_out)
 {
@@ -198,6 +337,9 @@ __global__ void empty_rows_kernel(int64_t rows, float* m_out, float* l_out)
 }
 
 namespace {
+
+// longest row held in registers (one workgroup of 512 lanes x 32 logits)
+constexpr int64_t kRegisterCols = 16384;
 
 template <bool BF16, bool VEC, int TPR, int N, int BLOCK>
 hipError_t launch_one(const RowSoftmaxArgs& a)
@@ -225,8 +367,43 @@ hipError_t launch_blocks(const RowSoftmaxArgs& a)
 }
 
 template <bool BF16, bool VEC>
+hipError_t launch_stream(const RowSoftmaxArgs& a)
+{
+    constexpr int WG = 512;
+    const dim3 grid((unsigned)a.rows), blk(WG);
+    switch (a.block) {
+    case 1:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 1, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    case 2:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 2, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    case 4:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 4, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    case 8:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 8, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    case 16:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 16, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    default:
+        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 32, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
+                           a.m_out, a.l_out);
+        break;
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16, bool VEC>
 hipError_t launch_cols(const RowSoftmaxArgs& a)
 {
+    if (a.cols > kRegisterCols) return launch_stream<BF16, VEC>(a);
     // Smallest per-lane register count that covers the row: one wave per row
     // up to 2048 logits, one workgroup of 4 (or 8) waves beyond.
     const int64_t c = a.cols;
@@ -258,14 +435,14 @@ hipError_t launch_row_softmax(const RowSoftmaxArgs& a)
     return vec ? launch_cols<false, true>(a) : launch_cols<false, false>(a);
 }
 
-int64_t row_softmax_max_cols() { return 16384; }
+int64_t row_softmax_max_cols() { return INT64_MAX; }
 
 int64_t row_softmax_rows_per_launch_limit(int64_t cols, bool bf16)
 {
     // grid.x is at most 2^31 - 1 workgroups; wave-per-row configurations put
     // four rows in a workgroup
     (void)bf16;
-    const int64_t rpw = cols <= 2048 ? 4 : 1;
+    const int64_t rpw = cols <= 2048 ? 4 : 1;  // the streaming path (cols > 16384) takes one row per workgroup
     return (int64_t)0x7fffffff * rpw;
 }
 
