@@ -71,9 +71,10 @@ STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) t
     "attn_nc": ["attn_fwd_kernel<64, 128, 8, true>"],
     "attn_causal": ["attn_fwd_kernel<128, 64, 8, true>"],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
+    "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
-                "attn_causal": "attn_fwd", "decode": "decode"}
+                "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax"}
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, command: str):
@@ -138,7 +139,7 @@ def main():
                     help="keep warming up until this much wall time has passed (at least --warmup steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode")
+    ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,softmax_long_f32")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -184,6 +185,15 @@ def main():
                            kind="hbm", kernel="row_softmax",
                            workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
             log(f"inputs {name} ready ({time.perf_counter() - t0:.1f}s)")
+    if "softmax_long_f32" in stages:
+        w = inputs.WORKLOADS["softmax_long"]  # rows longer than 16384: the two-read streaming path
+        R, C = w["rows"], w["cols"]
+        x = inputs.logits(R, C, 30.0, 206, "f32").to(dev)
+        y = torch.empty_like(x)
+        S["softmax_long_f32"] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 12,
+                                     kind="hbm", kernel="row_softmax",
+                                     workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block 8, two reads + one write")
+        log(f"inputs softmax_long_f32 ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_nc" in stages:
         w = inputs.WORKLOADS["attn_noncausal"]
         B, H, Sq, D = w["B"], w["H"], w["S"], w["D"]
@@ -228,7 +238,8 @@ def main():
         del a, b
 
     stream = torch.cuda.current_stream(dev)
-    names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode") if n in S]
+    names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode", "softmax_long_f32")
+             if n in S]
 
     def step(events=None):
         for n in names:
