@@ -72,9 +72,11 @@ STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) t
     "attn_causal": ["attn_fwd_kernel<128, 64, 8, true>"],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
     "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512>"],
+    "decode_fused": ["decode_fused_kernel<128, 4, true>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
-                "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax"}
+                "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax",
+                "decode_fused": "decode"}
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, command: str):
@@ -139,7 +141,8 @@ def main():
                     help="keep warming up until this much wall time has passed (at least --warmup steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--stages", default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,softmax_long_f32")
+    ap.add_argument("--stages",
+                    default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,decode_fused,softmax_long_f32")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -212,7 +215,7 @@ def main():
                                 units=4 * B * H * D * Sq * (Sq + 1) // 2, kind="mfma", kernel="attn_fwd",
                                 workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 causal")
         log(f"inputs attn_causal ready ({time.perf_counter() - t0:.1f}s)")
-    if "decode" in stages:
+    if "decode" in stages or "decode_fused" in stages:
         w = inputs.WORKLOADS["decode_splitkv"]
         B, H, Lmax, D, ns = w["B"], w["H"], w["Lmax"], w["D"], w["num_splits"]
         q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=501)
@@ -225,6 +228,13 @@ def main():
                                                                out=od)),
                            units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode",
                            workload=f"decode B{B} H{H} Lmax{Lmax} D{D} bf16 splits{ns} sum(kv_len)={tot}")
+        if "decode_fused" in stages:
+            of = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+            S["decode_fused"] = dict(fn=(lambda: tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=ns, out=of)),
+                                     units=S["decode"]["units"], kind="hbm", kernel="decode",
+                                     workload=S["decode"]["workload"] + ", one launch")
+        if "decode" not in stages:
+            del S["decode"]
         log(f"inputs decode ready ({time.perf_counter() - t0:.1f}s)")
 
     if args.calibrate_copy:
@@ -238,8 +248,8 @@ def main():
         del a, b
 
     stream = torch.cuda.current_stream(dev)
-    names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode", "softmax_long_f32")
-             if n in S]
+    names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode", "decode_fused",
+                         "softmax_long_f32") if n in S]
 
     def step(events=None):
         for n in names:

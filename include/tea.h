@@ -125,6 +125,22 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32
                         size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_fused -- the same decode in one launch and with no workspace:
+ * one workgroup of 16 waves per (batch, head); the num_splits chunks are the
+ * leaves of a balanced binary tree of 64 leaves (those at or past num_splits
+ * are empty), each wave computes four of them and combines them, and the
+ * waves' states are combined through LDS ("Online Softmax" (metalworking),
+ * Recognition guide: the Apple decode kernels merge partial results from
+ * different simdgroups).  Same chunk bounds, tree and combine as
+ * attn_decode_splitkv; the two agree up to rounding.
+ *   Arguments as for attn_decode_splitkv, without the workspace;
+ *   num_splits 1 .. 64 (else TEA_EINVAL).
+ * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
+ */
+int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B, int H,
+                      int Lmax, int D, int num_splits, float scale, int out_dtype, void* stream);
+
+/*
  * merge_partials -- merge S partial softmax states per row into one, by a
  * balanced pairwise tree over the partial index (for S <= 64; for larger S,
  * contiguous groups of ceil(S/64) are folded in order first), with no atomics

@@ -108,6 +108,25 @@ def test_decode_validation(lib):
     assert call(B=0) == tea.TEA_OK
 
 
+def test_decode_fused_validation(lib):
+    f = lib.attn_decode_fused
+    P = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+         ctypes.c_void_p(0x50000)]
+
+    def call(B=2, H=2, Lmax=100, D=128, S=64, scale=0.1, od=tea.TEA_BF16, ptrs=P):
+        return f(*ptrs, B, H, Lmax, D, S, scale, od, NULL)
+
+    assert call(S=0) == tea.TEA_EINVAL
+    assert call(S=65) == tea.TEA_EINVAL  # 64 leaves at most
+    assert call(D=96) == tea.TEA_EUNSUPPORTED
+    assert call(Lmax=0) == tea.TEA_EINVAL
+    assert call(scale=float("inf")) == tea.TEA_EINVAL
+    assert call(od=7) == tea.TEA_EINVAL
+    assert call(ptrs=[P[0], P[1], P[2], P[3], NULL]) == tea.TEA_EINVAL
+    assert call(ptrs=[ODD, *P[1:]]) == tea.TEA_EINVAL
+    assert call(H=0) == tea.TEA_OK
+
+
 def test_merge_validation(lib):
     f = lib.merge_partials
     m, l, O, o = (ctypes.c_void_p(a) for a in (0x10000, 0x20000, 0x30000, 0x90000))

@@ -6,7 +6,8 @@ at full size on sampled (b, h) pairs and by properties at any size; lengths
 at chunk and tile edges (including L < 64, where chunks are empty, and
 L = 0); other split counts.  Merge: random partials against the merged state
 written out directly; the empty state as identity; all-empty rows; any S and
-D; agreement of different tree shapes up to rounding.
+D; agreement of different tree shapes up to rounding.  The single-launch
+decode against the oracle and against the two-launch form.
 """
 import math
 
@@ -78,6 +79,54 @@ def test_decode_full_size_sampled():
     got = np.stack([to_np(o[b, h]) for b, h in pairs])
     err = check_attention(got, ref, "decode full size")
     print(f"decode: max abs err {err:.3e} over {len(pairs)} (b, h) pairs; kv_len={kv.tolist()}")
+
+
+# ---- attn_decode_fused: the single-launch form ------------------------------
+
+@pytest.mark.parametrize("lengths", [[1, 2, 63, 64], [65, 511, 512, 513], [1000, 4096, 32767, 32768], [0, 5, 0, 70]])
+@pytest.mark.parametrize("splits", [1, 3, 16, 64])
+def test_decode_fused_edge_lengths(lengths, splits):
+    say(f"decode fused lengths={lengths} splits={splits}")
+    B, H, D = len(lengths), 3, 128
+    Lmax = max(max(lengths), 1)
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=sum(lengths) + splits + 7, kv_len=np.array(lengths))
+    scale = 1.0 / math.sqrt(D)
+    qd, Kd, Vd, kvd = q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV)
+    o = tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=splits, scale=scale)
+    o32 = tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=splits, scale=scale, out_dtype=torch.float32)
+    o2 = tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=splits, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    ref = _decode_ref(q, K, V, kv.numpy(), scale, pairs)
+    check_attention(to_np(o).reshape(-1, D), ref, f"fused lengths={lengths} splits={splits}")
+    # the two forms share chunk bounds, tree and combine; only the order of
+    # the fp32 sums inside a chunk differs
+    assert float((o32 - o2).abs().max()) <= 1e-5
+    for b in range(B):
+        if lengths[b] == 0:
+            assert torch.all(o[b] == 0)
+
+
+def test_decode_fused_d64_full_size_sampled():
+    say("decode fused D=64 fp32 out; full-size workload sampled")
+    q, K, V, kv = inputs.decode_inputs(3, 4, 3000, 64, seed=19, kv_len=np.array([3000, 17, 1234]))
+    o = tea.attn_decode_fused(q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV), num_splits=64, scale=0.125,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(3) for h in range(4)]
+    check_attention(to_np(o).reshape(-1, 64), _decode_ref(q, K, V, kv.numpy(), 0.125, pairs), "fused D64", atol=2e-3)
+    w = inputs.WORKLOADS["decode_splitkv"]
+    B, H, Lmax, D, S = w["B"], w["H"], w["Lmax"], w["D"], w["num_splits"]
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=501)
+    scale = 1.0 / math.sqrt(D)
+    qd, Kd, Vd, kvd = q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV)
+    o = tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=S, scale=scale)
+    o2 = tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=S, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    pairs = [(0, 0), (B - 1, H - 1), (int(np.argmax(kv.numpy())), 5), (int(np.argmin(kv.numpy())), 9)]
+    got = np.stack([to_np(o[b, h]) for b, h in pairs])
+    check_attention(got, _decode_ref(q, K, V, kv.numpy(), scale, pairs), "fused full size")
 
 
 # ---- merge_partials ----------------------------------------------------------

@@ -16,7 +16,8 @@ import threading
 import torch
 
 __all__ = [
-    "row_softmax", "attn_fwd", "attn_decode_splitkv", "attn_decode_workspace_bytes", "merge_partials",
+    "row_softmax", "attn_fwd", "attn_decode_splitkv", "attn_decode_workspace_bytes", "attn_decode_fused",
+    "merge_partials",
     "TeaError", "library_path", "load_library",
     "TEA_OK", "TEA_EINVAL", "TEA_EUNSUPPORTED", "TEA_EHIP", "TEA_F32", "TEA_BF16",
 ]
@@ -29,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libtea.so")
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("row_softmax", "attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "merge_partials",
+EXPORTS = ("row_softmax", "attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_fused",
+           "merge_partials",
            "tea_status_string", "tea_abi_version")
 
 
@@ -62,6 +64,8 @@ def load_library():
             lib.attn_decode_workspace_bytes.restype = SZ
             lib.attn_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, P]
             lib.attn_decode_splitkv.restype = I
+            lib.attn_decode_fused.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+            lib.attn_decode_fused.restype = I
             lib.merge_partials.argtypes = [P, P, P, I64, I, I, P, P, P, I, I, P]
             lib.merge_partials.restype = I
             lib.tea_status_string.argtypes = [I]
@@ -153,6 +157,25 @@ def attn_decode_splitkv(q, k, v, kv_len, num_splits: int = 64, scale: float | No
     _check("attn_decode_splitkv", load_library().attn_decode_splitkv(
         _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o), B, H, Lmax, D, int(num_splits), float(scale),
         _dcode(o.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    return o
+
+
+def attn_decode_fused(q, k, v, kv_len, num_splits: int = 64, scale: float | None = None,
+                      out_dtype=torch.bfloat16, out: torch.Tensor | None = None):
+    """Split-KV decode in one launch, no workspace (num_splits <= 64): q
+    [B,H,1,D], k/v [B,H,Lmax,D] bf16, kv_len [B] int32 (device).  Returns
+    O [B,H,D]."""
+    B, H, _, D = q.shape
+    Lmax = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, H, D), dtype=out_dtype, device=q.device) if out is None else out
+    _dev(q, k, v, kv_len, o)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    _check("attn_decode_fused", load_library().attn_decode_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o), B, H, Lmax, D, int(num_splits), float(scale),
+        _dcode(o.dtype), _stream(q)))
     return o
 
 

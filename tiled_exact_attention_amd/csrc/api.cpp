@@ -121,6 +121,24 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32
     return status_of(tea::launch_decode(a));
 }
 
+int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B, int H,
+                      int Lmax, int D, int num_splits, float scale, int out_dtype, void* stream)
+{
+    if (B < 0 || H < 0 || Lmax < 1 || D <= 0) return TEA_EINVAL;
+    if (num_splits < 1 || num_splits > tea::decode_fused_max_splits()) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (!good_scale(scale)) return TEA_EINVAL;
+    if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H == 0) return TEA_OK;
+    if ((int64_t)B * H > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if (!q || !k || !v || !kv_len || !o) return TEA_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(o, 4))
+        return TEA_EINVAL;
+    tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, nullptr, nullptr,
+                      nullptr, (hipStream_t)stream};
+    return status_of(tea::launch_decode_fused(a));
+}
+
 int merge_partials(const float* m, const float* l, const float* O, int64_t N, int S, int D, float* m_out,
                    float* l_out, void* O_out, int out_dtype, int normalize, void* stream)
 {

@@ -47,44 +47,34 @@ __device__ __forceinline__ void combine8(float& m1, float& l1, float* O1, float 
     m1 = m;
 }
 
-// One wave per (b, h, chunk): a wave streams its chunk's keys on its own, so
-// there is no LDS and no barrier, and many chunks are in flight per CU.
+// the same combine for one dimension
+__device__ __forceinline__ void combine8_1(float& m1, float& l1, float& O1, float m2, float l2, float O2)
+{
+    const float m = fmaxf(m1, m2);
+    const float mu = guard_max(m);
+    const float a1 = exp2_hw(m1 - mu), a2 = exp2_hw(m2 - mu);
+    l1 = fmaf(a1, l1, a2 * l2);
+    O1 = fmaf(a1, O1, a2 * O2);
+    m1 = m;
+}
+
+// The partial state of one chunk [k0, k1) of one (b, h): each group of D/8
+// lanes owns a key slot and 8 dimensions; per step a slot takes U keys,
+// computes their scores (DPP reduction across the group) and folds them into
+// its running (m, l, O) with the online recurrence; the slots' states are then
+// merged by a butterfly over lane groups (both partners combine (lower slot,
+// upper slot) in that order).  On return every lane group holds the chunk's
+// state for its 8 dimensions; maxima are in base-two units.
 template <int D, int U>
-__global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ q,
-                                                             const uint16_t* __restrict__ k,
-                                                             const uint16_t* __restrict__ v,
-                                                             const int32_t* __restrict__ kv_len, int64_t nchunks, int H,
-                                                             int Lmax, int S, float scale_log2, float* __restrict__ ws_m,
-                                                             float* __restrict__ ws_l, float* __restrict__ ws_O)
+__device__ __forceinline__ void chunk_state(const float* qs, const u32x4_t* kb, const u32x4_t* vb, int64_t k0,
+                                            int64_t k1, int lane, float& m, float& l, float* O)
 {
     constexpr int LPK = D / 8;     // lanes per key
     constexpr int KPW = 64 / LPK;  // key slots per wave
-    const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk handled by this wave
-    if (gw >= nchunks) return;  // whole wave
-    const int slot = lane / LPK, dl = lane % LPK;
-    const int c = (int)(gw % S);
-    const int64_t bh = gw / S;
-    const int b = (int)(bh / H);
-    int L = kv_len[b];
-    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-    const int64_t k0 = (int64_t)c * L / S, k1 = (int64_t)(c + 1) * L / S;
-
-    // q with scale * log2(e) folded in once: scores come out in base two
-    float qs[8];
-    {
-        const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(q + bh * D + dl * 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            qs[2 * j] = bf16_lo(w4[j]) * scale_log2;
-            qs[2 * j + 1] = bf16_hi(w4[j]) * scale_log2;
-        }
-    }
-    const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k + bh * (int64_t)Lmax * D + dl * 8);
-    const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v + bh * (int64_t)Lmax * D + dl * 8);
-    constexpr int RS = D / 8;  // row stride in 16-byte units
-
-    float m = kNegInf, l = 0.0f, O[8];
+    constexpr int RS = D / 8;      // row stride in 16-byte units
+    const int slot = lane / LPK;
+    m = kNegInf;
+    l = 0.0f;
 #pragma unroll
     for (int d = 0; d < 8; ++d) O[d] = 0.0f;
 
@@ -135,8 +125,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
         m = mn;
     }
 
-    // merge the key slots of this wave (butterfly over lane groups; both
-    // partners combine (lower slot, upper slot) in that order)
 #pragma unroll
     for (int x = LPK; x < 64; x <<= 1) {
         float mp = __shfl_xor(m, x), lp = __shfl_xor(l, x), Op[8];
@@ -156,6 +144,50 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
             combine8(m, l, O, mp, lp, Op);
         }
     }
+}
+
+// q of (b, h) with scale * log2(e) folded in once (scores come out in base
+// two): lane group member dl holds dimensions 8 dl .. 8 dl + 8
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* q, int64_t bh, int dl, float scale_log2, float* qs)
+{
+    const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(q + bh * D + dl * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        qs[2 * j] = bf16_lo(w4[j]) * scale_log2;
+        qs[2 * j + 1] = bf16_hi(w4[j]) * scale_log2;
+    }
+}
+
+// Launch 1 of the two-launch form: one wave per (b, h, chunk).  A wave streams
+// its chunk's keys on its own, so there is no LDS and no barrier, and many
+// chunks are in flight per CU.
+template <int D, int U>
+__global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             const int32_t* __restrict__ kv_len, int64_t nchunks, int H,
+                                                             int Lmax, int S, float scale_log2, float* __restrict__ ws_m,
+                                                             float* __restrict__ ws_l, float* __restrict__ ws_O)
+{
+    constexpr int LPK = D / 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // chunk handled by this wave
+    if (gw >= nchunks) return;  // whole wave
+    const int dl = lane % LPK;
+    const int c = (int)(gw % S);
+    const int64_t bh = gw / S;
+    const int b = (int)(bh / H);
+    int L = kv_len[b];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+    const int64_t k0 = (int64_t)c * L / S, k1 = (int64_t)(c + 1) * L / S;
+
+    float qs[8];
+    load_q<D>(q, bh, dl, scale_log2, qs);
+    const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k + bh * (int64_t)Lmax * D + dl * 8);
+    const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v + bh * (int64_t)Lmax * D + dl * 8);
+    float m, l, O[8];
+    chunk_state<D, U>(qs, kb, vb, k0, k1, lane, m, l, O);
     if (lane < LPK) {
         const int64_t p = gw;  // = bh * S + c
         if (lane == 0) {
@@ -165,6 +197,107 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(const uint16_t* __r
         f32x4v_t* dst = reinterpret_cast<f32x4v_t*>(ws_O + p * D + dl * 8);
         dst[0] = f32x4v_t{O[0], O[1], O[2], O[3]};
         dst[1] = f32x4v_t{O[4], O[5], O[6], O[7]};
+    }
+}
+
+// Single-launch form: one workgroup of kFW waves per (b, h); the chunks are
+// the leaves 0 .. 4 kFW - 1 of a balanced binary tree (leaves at or past
+// num_splits are empty), wave w takes leaves 4w .. 4w + 3 and combines them
+// as the tree's two lowest levels, and the waves' states are combined through
+// LDS as its upper levels.  The tree and the combine are those of the
+// two-launch form (whose merge is the same balanced tree over the partial
+// index); within a chunk a slot takes 4 keys per step instead of 8, to fit
+// 16 waves' registers, so the two agree up to rounding.  This form needs no
+// workspace and one launch, as the Apple decode kernels merge their
+// simdgroups ("Online Softmax" (metalworking), Recognition guide), but all
+// of a (b, h) runs on one CU.
+constexpr int kFW = 16;  // waves per workgroup: 64 leaves
+
+template <int D, int U, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kFW) void decode_fused_kernel(const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ k,
+                                                                const uint16_t* __restrict__ v,
+                                                                const int32_t* __restrict__ kv_len, int H, int Lmax,
+                                                                int S, float scale_log2, void* __restrict__ o)
+{
+    constexpr int LPK = D / 8;
+    __shared__ float sm[kFW], sl[kFW], sO[kFW][D];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int dl = lane % LPK;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / H);
+    int L = kv_len[b];
+    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+
+    float qs[8];
+    load_q<D>(q, bh, dl, scale_log2, qs);
+    const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(k + bh * (int64_t)Lmax * D + dl * 8);
+    const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(v + bh * (int64_t)Lmax * D + dl * 8);
+
+    // leaves 4w .. 4w+3: ((4w, 4w+1), (4w+2, 4w+3))
+    float m2[2], l2[2], O2[2][8];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        float ma = kNegInf, la = 0.0f, Oa[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) Oa[d] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = 4 * w + 2 * pr + e;
+            float mc = kNegInf, lc = 0.0f, Oc[8];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) Oc[d] = 0.0f;
+            if (c < S) {
+                const int64_t k0 = (int64_t)c * L / S, k1 = (int64_t)(c + 1) * L / S;
+                chunk_state<D, U>(qs, kb, vb, k0, k1, lane, mc, lc, Oc);
+            }
+            if (e == 0) {
+                ma = mc;
+                la = lc;
+#pragma unroll
+                for (int d = 0; d < 8; ++d) Oa[d] = Oc[d];
+            } else {
+                combine8(ma, la, Oa, mc, lc, Oc);
+            }
+        }
+        m2[pr] = ma;
+        l2[pr] = la;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) O2[pr][d] = Oa[d];
+    }
+    combine8(m2[0], l2[0], O2[0], m2[1], l2[1], O2[1]);
+    if (lane < LPK) {
+        if (lane == 0) {
+            sm[w] = m2[0];
+            sl[w] = l2[0];
+        }
+#pragma unroll
+        for (int d = 0; d < 8; ++d) sO[w][dl * 8 + d] = O2[0][d];
+    }
+    __syncthreads();
+
+    // upper levels: thread d < D combines the kFW wave states for dimension d
+    const int d = threadIdx.x;
+    if (d < D) {
+        float mw[kFW], lw[kFW], Ow[kFW];
+#pragma unroll
+        for (int i = 0; i < kFW; ++i) {
+            mw[i] = sm[i];
+            lw[i] = sl[i];
+            Ow[i] = sO[i][d];
+        }
+#pragma unroll
+        for (int span = 1; span < kFW; span <<= 1)
+#pragma unroll
+            for (int i = 0; i < kFW; i += 2 * span) combine8_1(mw[i], lw[i], Ow[i], mw[i + span], lw[i + span], Ow[i + span]);
+        const float inv = lw[0] > 0.0f ? 1.0f / lw[0] : 0.0f;
+        const float val = Ow[0] * inv;
+        if constexpr (OUT_BF16) {
+            bf16x2_t pk = {(__bf16)val, (__bf16)0.0f};
+            static_cast<uint16_t*>(o)[bh * D + d] = (uint16_t)(__builtin_bit_cast(unsigned, pk) & 0xffffu);
+        } else {
+            static_cast<float*>(o)[bh * D + d] = val;
+        }
     }
 }
 
@@ -196,5 +329,30 @@ hipError_t launch_decode(const DecodeArgs& a)
                 true, a.stream};
     return launch_merge_base2(m);
 }
+
+hipError_t launch_decode_fused(const DecodeArgs& a)
+{
+    const dim3 grid((unsigned)((int64_t)a.B * a.H)), block(64 * kFW);
+    const float scale_log2 = a.scale * kLog2eHi;
+    const uint16_t *q = (const uint16_t*)a.q, *k = (const uint16_t*)a.k, *v = (const uint16_t*)a.v;
+    if (a.D == 128) {
+        if (a.out_bf16)
+            hipLaunchKernelGGL((decode_fused_kernel<128, 4, true>), grid, block, 0, a.stream, q, k, v, a.kv_len, a.H,
+                               a.Lmax, a.num_splits, scale_log2, a.o);
+        else
+            hipLaunchKernelGGL((decode_fused_kernel<128, 4, false>), grid, block, 0, a.stream, q, k, v, a.kv_len, a.H,
+                               a.Lmax, a.num_splits, scale_log2, a.o);
+    } else {
+        if (a.out_bf16)
+            hipLaunchKernelGGL((decode_fused_kernel<64, 4, true>), grid, block, 0, a.stream, q, k, v, a.kv_len, a.H,
+                               a.Lmax, a.num_splits, scale_log2, a.o);
+        else
+            hipLaunchKernelGGL((decode_fused_kernel<64, 4, false>), grid, block, 0, a.stream, q, k, v, a.kv_len, a.H,
+                               a.Lmax, a.num_splits, scale_log2, a.o);
+    }
+    return hipGetLastError();
+}
+
+int decode_fused_max_splits() { return 4 * kFW; }
 
 }  // namespace tea

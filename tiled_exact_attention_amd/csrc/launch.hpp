@@ -51,6 +51,8 @@ struct DecodeArgs {
     hipStream_t stream;
 };
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_fused(const DecodeArgs& a);  // ws_* unused
+int decode_fused_max_splits();
 size_t decode_workspace_bytes(int B, int H, int D, int num_splits);
 
 struct AttnArgs {
