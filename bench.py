@@ -37,7 +37,8 @@ BF16_PEAK_TFLOPS = 2516.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "row_softmax": ["tiled_exact_attention_amd/csrc/softmax.hip", "tiled_exact_attention_amd/csrc/common.hpp"],
-    "attn_fwd": ["tiled_exact_attention_amd/csrc/attn_fwd.hip", "tiled_exact_attention_amd/csrc/common.hpp"],
+    "attn_fwd": ["tiled_exact_attention_amd/csrc/attn_fwd.hip", "tiled_exact_attention_amd/csrc/merge.hip",
+                 "tiled_exact_attention_amd/csrc/common.hpp"],
     "decode": ["tiled_exact_attention_amd/csrc/decode.hip", "tiled_exact_attention_amd/csrc/merge.hip",
                "tiled_exact_attention_amd/csrc/common.hpp"],
 }
@@ -65,18 +66,21 @@ def measured_traffic(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-STAGE_KERNELS = {  # stage -> substrings of the kernel names (in launch order) that make up one launch
+STAGE_KERNELS = {  # stage -> kernels (in launch order) that make up one launch: a substring of the kernel
+    # name, or (substring, grid size in threads) where stages share a kernel
     "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256>"],
     "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
     "attn_nc": ["attn_fwd_kernel<64, 128, 8, true>"],
-    "attn_causal": ["attn_fwd_kernel<128, 64, 8, true>"],
+    "attn_causal": [("attn_fwd_kernel<128, 64, 8, true>", 2048 * 512)],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
     "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512>"],
     "decode_fused": ["decode_fused_kernel<128, 4, true>"],
+    "attn_lowocc": [("attn_fwd_kernel<128, 64, 8, true>", 32 * 512)],
+    "attn_lowocc_splitk": [("attn_fwd_kernel<128, 64, 8, true>", 512 * 512), "merge_kernel<false, true, true>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
                 "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax",
-                "decode_fused": "decode"}
+                "decode_fused": "decode", "attn_lowocc": "attn_fwd", "attn_lowocc_splitk": "attn_fwd"}
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, command: str):
@@ -95,8 +99,12 @@ def ingest_counters(fetch_csv: str, write_csv: str, command: str):
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
             if "copyBuffer" in name and int(r["Grid_Size"]) >= 65536:
                 copy = v
-            per[name].append(v)
+            per[(name, int(r["Grid_Size"]))].append(v)
         return per, copy
+
+    def match(per, part):
+        sub, grid = (part, None) if isinstance(part, str) else part
+        return [k for k in per if sub in k[0] and (grid is None or k[1] == grid)]
 
     fetch, fcopy = load(fetch_csv)
     write, wcopy = load(write_csv)
@@ -108,8 +116,8 @@ def ingest_counters(fetch_csv: str, write_csv: str, command: str):
         fk = wk = 0.0
         found = True
         for sub in parts:
-            fn = [k for k in fetch if sub in k]
-            wn = [k for k in write if sub in k]
+            fn = match(fetch, sub)
+            wn = match(write, sub)
             if not fn or not wn:
                 found = False
                 break
@@ -142,7 +150,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stages",
-                    default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,decode_fused,softmax_long_f32")
+                    default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,decode_fused,softmax_long_f32,"
+                            "attn_lowocc,attn_lowocc_splitk")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -206,6 +215,21 @@ def main():
                             units=4 * B * H * Sq * Sq * D, kind="mfma", kernel="attn_fwd",
                             workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 non-causal")
         log(f"inputs attn_nc ready ({time.perf_counter() - t0:.1f}s)")
+    if "attn_lowocc" in stages or "attn_lowocc_splitk" in stages:
+        w = inputs.WORKLOADS["attn_lowocc"]
+        B, H, Sq, Sk, D, ns = w["B"], w["H"], w["Sq"], w["Sk"], w["D"], w["num_splits"]
+        q, k, v = (t.to(dev) for t in inputs.qkv(B, H, Sq, Sk, D, seed=601))
+        o = torch.empty_like(q)
+        wl = f"attn_fwd B{B} H{H} Sq{Sq} Sk{Sk} D{D} bf16 non-causal ({(Sq + 255) // 256 * B * H} query blocks)"
+        if "attn_lowocc" in stages:
+            S["attn_lowocc"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, out=o)),
+                                    units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", workload=wl)
+        if "attn_lowocc_splitk" in stages:
+            wsk = torch.empty(tea.attn_fwd_splitk_workspace_bytes(B, H, Sq, D, ns), dtype=torch.uint8, device=dev)
+            S["attn_lowocc_splitk"] = dict(
+                fn=(lambda q=q, k=k, v=v, o=o, wsk=wsk, ns=ns: tea.attn_fwd_splitk(q, k, v, ns, workspace=wsk, out=o)),
+                units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", workload=wl + f", {ns} KV splits")
+        log(f"inputs attn_lowocc ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_causal" in stages:
         w = inputs.WORKLOADS["attn_causal"]
         B, H, Sq, D = w["B"], w["H"], w["S"], w["D"]
@@ -224,13 +248,15 @@ def main():
         ws = torch.empty(tea.attn_decode_workspace_bytes(B, H, D, ns), dtype=torch.uint8, device=dev)
         od = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
         tot = int(kv.sum())
-        S["decode"] = dict(fn=(lambda: tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=ns, workspace=ws,
+        S["decode"] = dict(fn=(lambda qd=qd, Kd=Kd, Vd=Vd, kvd=kvd, ns=ns, ws=ws, od=od:
+                               tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=ns, workspace=ws,
                                                                out=od)),
                            units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode",
                            workload=f"decode B{B} H{H} Lmax{Lmax} D{D} bf16 splits{ns} sum(kv_len)={tot}")
         if "decode_fused" in stages:
             of = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
-            S["decode_fused"] = dict(fn=(lambda: tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=ns, out=of)),
+            S["decode_fused"] = dict(fn=(lambda qd=qd, Kd=Kd, Vd=Vd, kvd=kvd, ns=ns, of=of:
+                                         tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=ns, out=of)),
                                      units=S["decode"]["units"], kind="hbm", kernel="decode",
                                      workload=S["decode"]["workload"] + ", one launch")
         if "decode" not in stages:
@@ -249,7 +275,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     names = [n for n in ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode", "decode_fused",
-                         "softmax_long_f32") if n in S]
+                         "softmax_long_f32", "attn_lowocc", "attn_lowocc_splitk") if n in S]
 
     def step(events=None):
         for n in names:

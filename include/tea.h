@@ -95,6 +95,32 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
              float scale, int causal, int out_dtype, float* lse_out, void* stream);
 
 /*
+ * attn_fwd_splitk_workspace_bytes -- bytes of workspace attn_fwd_splitk needs
+ * for these sizes (0 for invalid sizes).
+ */
+size_t attn_fwd_splitk_workspace_bytes(int B, int H, int Sq, int D, int num_splits);
+
+/*
+ * attn_fwd_splitk -- attn_fwd with each query block's KV tiles split into
+ * num_splits contiguous ranges, one workgroup each, for shapes with too few
+ * query blocks to fill the GPU.  Each range yields a partial state (m, l, O)
+ * per query, and the partials are merged by the associative combine, as
+ * merge_partials does ("The Online Softmax" (curionode), One pass, exactly:
+ * partial results merge in any order or tree, or across devices).
+ *   Arguments as for attn_fwd, plus
+ *   num_splits 1 .. 64 (else TEA_EINVAL); tile ranges may be empty (their
+ *            partial is the empty state);
+ *   workspace device memory of at least attn_fwd_splitk_workspace_bytes(),
+ *            16-byte aligned, owned by the caller, overlapping no other
+ *            argument; concurrent calls need separate workspaces.
+ * The result equals attn_fwd's up to rounding.
+ * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
+ */
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq, int Sk, int D,
+                    float scale, int causal, int num_splits, int out_dtype, float* lse_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of workspace attn_decode_splitkv needs
  * for these sizes (0 for invalid sizes).
  */

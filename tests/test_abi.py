@@ -85,6 +85,28 @@ def test_attn_fwd_validation(lib):
     assert call(B=0) == tea.TEA_OK
 
 
+def test_attn_fwd_splitk_validation(lib):
+    f = lib.attn_fwd_splitk
+    A = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)]
+    W = ctypes.c_void_p(0x1000000)
+    need = lib.attn_fwd_splitk_workspace_bytes(1, 1, 8, 64, 4)
+    assert need >= 8 * 4 * (64 + 2) * 4
+    assert lib.attn_fwd_splitk_workspace_bytes(1, 1, 8, 64, 65) == 0
+
+    def call(ptrs=A, B=1, H=1, Sq=8, Sk=8, D=64, scale=0.125, causal=0, S=4, od=tea.TEA_BF16, ws=W, wsb=need):
+        return f(*ptrs, B, H, Sq, Sk, D, scale, causal, S, od, NULL, ws, wsb, NULL)
+
+    assert call(S=0) == tea.TEA_EINVAL
+    assert call(S=65) == tea.TEA_EINVAL
+    assert call(wsb=need - 1) == tea.TEA_EINVAL
+    assert call(ws=NULL) == tea.TEA_EINVAL
+    assert call(ws=ctypes.c_void_p(0x40000 + 64)) == tea.TEA_EINVAL  # workspace overlaps o
+    assert call(D=96) == tea.TEA_EUNSUPPORTED
+    assert call(causal=1, Sk=9) == tea.TEA_EUNSUPPORTED
+    assert call(scale=-1.0) == tea.TEA_EINVAL
+    assert call(B=0) == tea.TEA_OK
+
+
 def test_decode_validation(lib):
     f = lib.attn_decode_splitkv
     assert lib.attn_decode_workspace_bytes(16, 32, 128, 64) >= 16 * 32 * 64 * (128 + 2) * 4

@@ -175,6 +175,54 @@ def test_drifting_maximum(D, causal, rise):
           f"worst err/bound {np.max(err / lim):.3f} / {np.max(err32 / pb):.3f}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 3, 8, 64])
+def test_splitk_parity(D, causal, splits):
+    """attn_fwd_splitk: each query block's KV tiles split `splits` ways, the
+    partials merged by the combine.  Against the oracle, and against attn_fwd
+    up to rounding (fp32 outputs).  With 64 splits most tile ranges of the
+    early causal blocks are empty, so their partials are the empty state."""
+    S = 700
+    say(f"attn_fwd_splitk S={S} D={D} causal={causal} splits={splits}")
+    q, k, v = inputs.qkv(1, 3, S, S, D, seed=splits * 13 + D + int(causal))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = tea.attn_fwd_splitk(qd, kd, vd, splits, scale=scale, causal=causal, return_lse=True)
+    o32 = tea.attn_fwd_splitk(qd, kd, vd, splits, scale=scale, causal=causal, out_dtype=torch.float32)
+    r32 = tea.attn_fwd(qd, kd, vd, scale=scale, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, causal)
+    check_attention(to_np(o), O, f"splitk D={D} causal={causal} splits={splits}")
+    assert np.max(np.abs(to_np(lse) - L)) <= LSE_TOL
+    # the same weights, rounded to bf16 against a different reference per
+    # range: within the fp32-output bound of either against the oracle
+    bound = 2.0 ** -8 * np.abs(_np32(v)).max() + 1e-5
+    assert float((o32 - r32).abs().max()) <= bound
+
+
+def test_splitk_rectangular_and_full_size_sample():
+    """Non-causal Sq != Sk with a ragged last tile, and the low-occupancy
+    shape of the bench (B1 H8 Sq1024 Sk65536 D128, 16 splits) on sampled
+    rows."""
+    say("attn_fwd_splitk rectangular 129 x 2049")
+    q, k, v = inputs.qkv(2, 2, 129, 2049, 128, seed=77)
+    o = tea.attn_fwd_splitk(q.to(DEV), k.to(DEV), v.to(DEV), 5)
+    torch.cuda.synchronize()
+    O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), 1 / math.sqrt(128), False)
+    check_attention(to_np(o), O, "splitk 129x2049")
+    w = inputs.WORKLOADS["attn_lowocc"]
+    B, H, Sq, Sk, D, ns = w["B"], w["H"], w["Sq"], w["Sk"], w["D"], w["num_splits"]
+    say(f"attn_fwd_splitk B{B} H{H} Sq{Sq} Sk{Sk} D{D} splits {ns}")
+    q, k, v = inputs.qkv(B, H, Sq, Sk, D, seed=601)
+    o, lse = tea.attn_fwd_splitk(q.to(DEV), k.to(DEV), v.to(DEV), ns, return_lse=True)
+    torch.cuda.synchronize()
+    flat = np.array([bh * Sq + i for bh in range(B * H) for i in (0, 1, 31, 32, 500, Sq - 1)])
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), 1 / math.sqrt(D), False, rows=flat)
+    check_attention(to_np(o).reshape(-1, D)[flat], O, "splitk low occupancy")
+    assert np.max(np.abs(to_np(lse).reshape(-1)[flat] - L)) <= LSE_TOL
+
+
 def test_empty_keys_give_zero():
     say("attn_fwd Sk=0")
     q = torch.randn(1, 2, 10, 64, dtype=torch.bfloat16, device=DEV)

@@ -16,8 +16,8 @@ import threading
 import torch
 
 __all__ = [
-    "row_softmax", "attn_fwd", "attn_decode_splitkv", "attn_decode_workspace_bytes", "attn_decode_fused",
-    "merge_partials",
+    "row_softmax", "attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_workspace_bytes", "attn_decode_splitkv",
+    "attn_decode_workspace_bytes", "attn_decode_fused", "merge_partials",
     "TeaError", "library_path", "load_library",
     "TEA_OK", "TEA_EINVAL", "TEA_EUNSUPPORTED", "TEA_EHIP", "TEA_F32", "TEA_BF16",
 ]
@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libtea.so")
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("row_softmax", "attn_fwd", "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_fused",
+EXPORTS = ("row_softmax", "attn_fwd", "attn_fwd_splitk_workspace_bytes", "attn_fwd_splitk",
+           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_fused",
            "merge_partials",
            "tea_status_string", "tea_abi_version")
 
@@ -66,6 +67,10 @@ def load_library():
             lib.attn_decode_splitkv.restype = I
             lib.attn_decode_fused.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
             lib.attn_decode_fused.restype = I
+            lib.attn_fwd_splitk_workspace_bytes.argtypes = [I, I, I, I, I]
+            lib.attn_fwd_splitk_workspace_bytes.restype = SZ
+            lib.attn_fwd_splitk.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, SZ, P]
+            lib.attn_fwd_splitk.restype = I
             lib.merge_partials.argtypes = [P, P, P, I64, I, I, P, P, P, I, I, P]
             lib.merge_partials.restype = I
             lib.tea_status_string.argtypes = [I]
@@ -131,6 +136,33 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out_dtyp
         raise TypeError("q, k, v must be bfloat16")
     _check("attn_fwd", load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Sq, Sk, D, float(scale),
                                                int(bool(causal)), _dcode(o.dtype), _ptr(lse), _stream(q)))
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd_splitk_workspace_bytes(B: int, H: int, Sq: int, D: int, num_splits: int) -> int:
+    return int(load_library().attn_fwd_splitk_workspace_bytes(B, H, Sq, D, num_splits))
+
+
+def attn_fwd_splitk(q, k, v, num_splits: int, scale: float | None = None, causal: bool = False,
+                    out_dtype=torch.bfloat16, return_lse: bool = False, workspace: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None):
+    """attn_fwd with each query block's KV range split num_splits ways and the
+    partial states merged; same arguments as attn_fwd."""
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = attn_fwd_splitk_workspace_bytes(B, H, Sq, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    _dev(q, k, v, o, lse, workspace)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    _check("attn_fwd_splitk", load_library().attn_fwd_splitk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Sq, Sk, D, float(scale), int(bool(causal)), int(num_splits),
+        _dcode(o.dtype), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return (o, lse) if return_lse else o
 
 

@@ -85,6 +85,45 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
     return status_of(tea::launch_attn_fwd(a));
 }
 
+size_t attn_fwd_splitk_workspace_bytes(int B, int H, int Sq, int D, int num_splits)
+{
+    if (B < 0 || H < 0 || Sq < 0 || D <= 0 || num_splits < 1 || num_splits > 64) return 0;
+    return tea::attn_splitk_workspace_bytes(B, H, Sq, D, num_splits);
+}
+
+int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq, int Sk, int D,
+                    float scale, int causal, int num_splits, int out_dtype, float* lse_out, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0) return TEA_EINVAL;
+    if (num_splits < 1 || num_splits > 64) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (causal != 0 && causal != 1) return TEA_EINVAL;
+    if (!good_scale(scale)) return TEA_EINVAL;
+    if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
+    if (causal && Sq != Sk) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H * Sq == 0) return TEA_OK;
+    if ((int64_t)B * H * ((Sq + 255) / 256) * num_splits > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if (!q || !o || !workspace || (Sk > 0 && (!k || !v))) return TEA_EINVAL;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(workspace, 16))
+        return TEA_EINVAL;
+    if (lse_out && !aligned(lse_out, 4)) return TEA_EINVAL;
+    const size_t need = tea::attn_splitk_workspace_bytes(B, H, Sq, D, num_splits);
+    if (workspace_bytes < need) return TEA_EINVAL;
+    const size_t qb = (size_t)B * H * Sq * D * 2, kb = (size_t)B * H * Sk * D * 2;
+    const size_t ob = (size_t)B * H * Sq * D * (out_dtype == TEA_F32 ? 4 : 2);
+    if (overlap(o, ob, q, qb) || (Sk > 0 && (overlap(o, ob, k, kb) || overlap(o, ob, v, kb)))) return TEA_EINVAL;
+    if (overlap(workspace, need, o, ob) || overlap(workspace, need, q, qb) ||
+        (Sk > 0 && (overlap(workspace, need, k, kb) || overlap(workspace, need, v, kb))))
+        return TEA_EINVAL;
+    if (lse_out && (overlap(lse_out, (size_t)B * H * Sq * 4, o, ob) ||
+                    overlap(lse_out, (size_t)B * H * Sq * 4, workspace, need)))
+        return TEA_EINVAL;
+    tea::AttnArgs a{q, k, v, o, B, H, Sq, Sk, D, scale, causal == 1, out_dtype == TEA_BF16, lse_out,
+                    (hipStream_t)stream};
+    return status_of(tea::launch_attn_fwd_splitk(a, num_splits, workspace));
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int D, int num_splits)
 {
     if (B < 0 || H < 0 || D <= 0 || num_splits < 1 || num_splits > 1024) return 0;

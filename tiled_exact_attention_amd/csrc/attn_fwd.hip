@@ -118,7 +118,9 @@ template <int D, int BN, int NW, bool OUT_BF16>
 __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, void* __restrict__ o,
-                                                          float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal)
+                                                          float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal,
+                                                          int nsplit, float* __restrict__ pm, float* __restrict__ pl,
+                                                          float* __restrict__ pO)
 {
     static_assert(NW == 8, "two groups of four waves, one wave of each group per SIMD");
     // causal is a runtime flag: as a template parameter it made hipcc spill
@@ -146,8 +148,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     const int G = gridDim.x;
     const int bid = blockIdx.x;
     const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-    int qb = logical % nqb;
-    const int64_t bh = logical / nqb;
+    // split-K (nsplit > 1): workgroup `split` of a query block takes its
+    // share of the KV tiles and writes a partial state
+    const int split = logical % nsplit;
+    const int lq_block = logical / nsplit;
+    int qb = lq_block % nqb;
+    const int64_t bh = lq_block / nqb;
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
     const int q0 = qb * kBM;
     const int qrow = q0 + w * 32 + lq;
@@ -178,9 +184,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     float m = kNegInf, l = 0.0f;
 
     const int kend = CAUSAL ? (Sk < q0 + kBM ? Sk : q0 + kBM) : Sk;
-    const int ntiles = (kend + BN - 1) / BN;
+    const int nall = (kend + BN - 1) / BN;
+    // this workgroup's tiles: [t0, t0 + ntiles) of the query block's nall;
+    // t below is the index within that range and key0 = kbase + t * BN
+    const int t0 = (int)((int64_t)split * nall / nsplit);
+    const int ntiles = (int)((int64_t)(split + 1) * nall / nsplit) - t0;
+    const int kbase = t0 * BN;
     // tiles after tlast hold no key visible to any query of this wave
-    const int tlast = CAUSAL ? min(ntiles - 1, qlast / BN) : ntiles - 1;
+    const int tlast = !CAUSAL ? ntiles - 1 : (qlast < kbase ? -1 : min(ntiles - 1, (qlast - kbase) / BN));
 
     // ---- HBM -> LDS: lane `lane` of this wave's j-th load fills 16 bytes
     // at byte (w * DPW + j) * 1024 + 16 * lane of the tile, i.e. row
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     };
     // ---- softmax phase X(t) on S(t) (in sacc): vector work only ----------
     auto xphase = [&](int t) __attribute__((always_inline)) {
-        const int key0 = t * BN;
+        const int key0 = kbase + t * BN;
         const bool mask = (key0 + BN > Sk) || (CAUSAL && key0 + BN - 1 > q0 + w * 32);
         if (mask) {
             // key = key0 + 4h + off with off = kb*32 + 8*(r/4) + r%4 a constant;
@@ -355,9 +366,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 
     // ---- prologue: K(0), V(0), K(1); every wave computes its S(0) ----------
     if (ntiles > 0) {
-        dma(kp, sK[0], false, 0);
-        dma(vp, sV[0], true, 0);
-        if (ntiles > 1) dma(kp, sK[1], false, BN);
+        dma(kp, sK[0], false, kbase);
+        dma(vp, sV[0], true, kbase);
+        if (ntiles > 1) dma(kp, sK[1], false, kbase + BN);
     }
     wait_vmem();
     __syncthreads();
@@ -368,8 +379,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     // V(t-1) and K(t), whose last reader ran in slot 2t
     auto loads = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;
-        if (t + 1 < ntiles) dma(vp, sV[P ^ 1], true, (t + 1) * BN);
-        if (t + 2 < ntiles) dma(kp, sK[P], false, (t + 2) * BN);
+        if (t + 1 < ntiles) dma(vp, sV[P ^ 1], true, kbase + (t + 1) * BN);
+        if (t + 2 < ntiles) dma(kp, sK[P], false, kbase + (t + 2) * BN);
     };
     // X(t) then M(t) for one tile; P = t & 1 is a constant, so every LDS
     // address is a per-lane offset plus an immediate
@@ -397,8 +408,29 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     }
     if (grp == 0) __syncthreads();  // the barrier of group 1's extra slot
 
-    // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
     const float lt = l + xor32(l);
+    if (nsplit > 1) {
+        // ---- partial state for merge_partials: m (natural units), l and
+        // unnormalised O, [row, split] with row = (b, h, query) --------------
+        if (qrow < Sq) {
+            const int64_t pr = (bh * Sq + qrow) * nsplit + split;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + 8 * g + 4 * h;
+                    *reinterpret_cast<f32x4v_t*>(pO + pr * D + d) =
+                        f32x4v_t{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                }
+            if (h == 0) {
+                pm[pr] = lt > 0.0f ? m * kLn2 : kNegInf;
+                pl[pr] = lt;
+            }
+        }
+        return;
+    }
+
+    // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (qrow < Sq) {
         const int64_t orow = (bh * Sq + qrow) * (int64_t)D;
@@ -421,21 +453,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
 }
 
 template <int D, int BN, int NW>
-hipError_t launch_d(const AttnArgs& a)
+hipError_t launch_d(const AttnArgs& a, int nsplit, float* pm, float* pl, float* pO)
 {
     constexpr int BM = 32 * NW;
     const int nqb = (a.Sq + BM - 1) / BM;
-    const int64_t grid = (int64_t)nqb * a.H * a.B;
+    const int64_t grid = (int64_t)nqb * a.H * a.B * nsplit;
     const float c = a.scale * kLog2eHi;
     if (a.out_bf16)
         hipLaunchKernelGGL((attn_fwd_kernel<D, BN, NW, true>), dim3((unsigned)grid), dim3(64 * NW), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
-                           nqb, a.causal ? 1 : 0);
+                           nqb, a.causal ? 1 : 0, nsplit, pm, pl, pO);
     else
         hipLaunchKernelGGL((attn_fwd_kernel<D, BN, NW, false>), dim3((unsigned)grid), dim3(64 * NW), 0, a.stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Sq, a.Sk, c,
-                           nqb, a.causal ? 1 : 0);
+                           nqb, a.causal ? 1 : 0, nsplit, pm, pl, pO);
     return hipGetLastError();
+}
+
+hipError_t launch_any(const AttnArgs& a, int nsplit, float* pm, float* pl, float* pO)
+{
+    if (a.D == 128) return launch_d<128, 64, 8>(a, nsplit, pm, pl, pO);
+    return launch_d<64, 128, 8>(a, nsplit, pm, pl, pO);
 }
 
 }  // namespace
@@ -443,8 +481,32 @@ hipError_t launch_d(const AttnArgs& a)
 hipError_t launch_attn_fwd(const AttnArgs& a)
 {
     if ((int64_t)a.B * a.H * a.Sq == 0) return hipSuccess;
-    if (a.D == 128) return launch_d<128, 64, 8>(a);
-    return launch_d<64, 128, 8>(a);
+    return launch_any(a, 1, nullptr, nullptr, nullptr);
+}
+
+size_t attn_splitk_workspace_bytes(int B, int H, int Sq, int D, int nsplit)
+{
+    const size_t n = (size_t)B * H * Sq * nsplit;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return 2 * up(n * sizeof(float)) + up(n * D * sizeof(float));
+}
+
+hipError_t launch_attn_fwd_splitk(const AttnArgs& a, int nsplit, void* workspace)
+{
+    if ((int64_t)a.B * a.H * a.Sq == 0) return hipSuccess;
+    if (nsplit == 1) return launch_any(a, 1, nullptr, nullptr, nullptr);  // one range: the plain kernel
+    const size_t n = (size_t)a.B * a.H * a.Sq * nsplit;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = static_cast<char*>(workspace);
+    float* pm = reinterpret_cast<float*>(ws);
+    float* pl = reinterpret_cast<float*>(ws + up(n * 4));
+    float* pO = reinterpret_cast<float*>(ws + 2 * up(n * 4));
+    hipError_t e = launch_any(a, nsplit, pm, pl, pO);
+    if (e != hipSuccess) return e;
+    MergeArgs m{pm, pl, pO, (int64_t)a.B * a.H * a.Sq, nsplit, a.D, nullptr, nullptr, a.o, a.out_bf16, true,
+                a.stream};
+    m.lse_out = a.lse;
+    return launch_merge(m);
 }
 
 }  // namespace tea

@@ -33,6 +33,7 @@ struct MergeArgs {
     bool out_bf16;
     bool normalize;
     hipStream_t stream;
+    float* lse_out = nullptr;  // [N] nullable: m + log l (natural units), -inf for an empty state
 };
 hipError_t launch_merge(const MergeArgs& a);
 
@@ -68,5 +69,7 @@ struct AttnArgs {
     hipStream_t stream;
 };
 hipError_t launch_attn_fwd(const AttnArgs& a);
+size_t attn_splitk_workspace_bytes(int B, int H, int Sq, int D, int nsplit);
+hipError_t launch_attn_fwd_splitk(const AttnArgs& a, int nsplit, void* workspace);
 
 }  // namespace tea

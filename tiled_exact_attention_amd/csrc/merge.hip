@@ -51,7 +51,7 @@ template <bool BASE2, bool OUT_BF16, bool NORMALIZE>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                     const float* __restrict__ pO, int64_t N, int S, int D,
                                                     float* __restrict__ m_out, float* __restrict__ l_out,
-                                                    void* __restrict__ O_out)
+                                                    void* __restrict__ O_out, float* __restrict__ lse_out)
 {
     const int lane = threadIdx.x & 63;
     const int nslices = (D + kDV - 1) / kDV;
@@ -96,8 +96,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
 
     if (lane == 0) {
         if (d0 == 0) {
-            if (m_out) m_out[n] = BASE2 ? m * kLn2 : m;
+            const float mn = BASE2 ? m * kLn2 : m;
+            if (m_out) m_out[n] = mn;
             if (l_out) l_out[n] = l;
+            if (lse_out) lse_out[n] = l > 0.0f ? mn + __logf(l) : kNegInf;
         }
         const float inv = (NORMALIZE && l > 0.0f) ? 1.0f / l : (NORMALIZE ? 0.0f : 1.0f);
 #pragma unroll
@@ -124,17 +126,17 @@ hipError_t launch_merge_t(const MergeArgs& a)
     if (a.out_bf16) {
         if (a.normalize)
             hipLaunchKernelGGL((merge_kernel<BASE2, true, true>), grid, block, 0, a.stream, a.m, a.l, a.O, a.N, a.S,
-                               a.D, a.m_out, a.l_out, a.O_out);
+                               a.D, a.m_out, a.l_out, a.O_out, a.lse_out);
         else
             hipLaunchKernelGGL((merge_kernel<BASE2, true, false>), grid, block, 0, a.stream, a.m, a.l, a.O, a.N, a.S,
-                               a.D, a.m_out, a.l_out, a.O_out);
+                               a.D, a.m_out, a.l_out, a.O_out, a.lse_out);
     } else {
         if (a.normalize)
             hipLaunchKernelGGL((merge_kernel<BASE2, false, true>), grid, block, 0, a.stream, a.m, a.l, a.O, a.N, a.S,
-                               a.D, a.m_out, a.l_out, a.O_out);
+                               a.D, a.m_out, a.l_out, a.O_out, a.lse_out);
         else
             hipLaunchKernelGGL((merge_kernel<BASE2, false, false>), grid, block, 0, a.stream, a.m, a.l, a.O, a.N,
-                               a.S, a.D, a.m_out, a.l_out, a.O_out);
+                               a.S, a.D, a.m_out, a.l_out, a.O_out, a.lse_out);
     }
     return hipGetLastError();
 }
