@@ -73,7 +73,7 @@ STAGE_KERNELS = {  # stage -> kernels (in launch order) that make up one launch:
     # name, or (substring, grid size in threads) where stages share a kernel
     "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256>"],
     "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
-    "attn_nc": ["attn_fwd_kernel<64, 128, 8, true>"],
+    "attn_nc": ["attn_fwd_kernel<64, 64, 16, true>"],
     "attn_causal": [("attn_fwd_kernel<128, 64, 8, true>", 2048 * 512)],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
     "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512>"],

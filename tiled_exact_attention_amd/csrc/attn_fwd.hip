@@ -4,8 +4,10 @@
 // (curionode), One pass, exactly: blocks stream through fast memory and no
 // row of scores is ever stored).
 //
-// Workgroup: 8 waves, 256 queries (32 per wave), so each K/V tile staged in
-// LDS serves 256 queries; KV tiles of 64 keys, double-buffered.  Both products run on v_mfma_f32_32x32x16_bf16 in transposed form:
+// Workgroup: 32 queries per wave; 8 waves (256 queries) for head dimension
+// 128, 16 waves (512 queries) for 64, so each K/V tile staged in LDS serves
+// that many queries; KV tiles of 64 keys, double-buffered.  Both products
+// run on v_mfma_f32_32x32x16_bf16 in transposed form:
 //     S^T = K Q^T   (A = K tile from LDS, B = Q^T held in registers)
 //     O^T = V^T P^T (A = V^T tile from LDS, B = P^T straight from the S^T
 //                    accumulators)
@@ -81,14 +83,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
                  : "memory");
 }
 
-// D: head dimension; BN: keys per KV tile.  Two waves per SIMD.
+// D: head dimension; BN: keys per KV tile; NW: waves, 8 or 16 (two or four
+// per SIMD).
 //
-// Two groups of four waves per workgroup, one wave of each group on every
-// SIMD, take turns ("ping-pong"): while one group runs the matrix phase of a
+// Two groups of NW / 2 waves per workgroup, NW / 8 waves of each group on
+// every SIMD, take turns ("ping-pong"): while one group runs the matrix phase of a
 // tile (M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, MFMAs fed from LDS)
 // the other runs the softmax phase (X: row maximum, reference, exponentials,
-// P), which is vector work only.  A SIMD then overlaps one wave's MFMAs with
-// the other wave's vector instructions.  Each wave alternates X(t), M(t),
+// P), which is vector work only.  A SIMD then overlaps one group's MFMAs with
+// the other group's vector instructions; with 16 waves two waves of a group
+// share a SIMD, which doubles the vector issue rate of the softmax phase (a
+// single wave issues a vector instruction only every few cycles).  Each wave alternates X(t), M(t),
 // X(t+1), ...; group 1 runs one phase behind group 0, and every phase ends
 // at a workgroup barrier:
 //   slot 2t  : group 0 X(t)        group 1 M(t-1)
@@ -115,14 +120,14 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
 // relative, so the result equals that of the exact running maximum up to
 // rounding.
 template <int D, int BN, int NW, bool OUT_BF16>
-__global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, void* __restrict__ o,
                                                           float* __restrict__ lse, int Sq, int Sk, float c, int nqb, int causal,
                                                           int nsplit, float* __restrict__ pm, float* __restrict__ pl,
                                                           float* __restrict__ pO)
 {
-    static_assert(NW == 8, "two groups of four waves, one wave of each group per SIMD");
+    static_assert(NW == 8 || NW == 16, "two groups of NW / 2 waves, NW / 8 waves of each group per SIMD");
     // causal is a runtime flag: as a template parameter it made hipcc spill
     // the non-causal instantiation
     const bool CAUSAL = causal != 0;
@@ -130,18 +135,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     constexpr int NCH = D / 8;                    // 16-byte chunks per row
     constexpr int RPI = 1024 / (2 * D);           // rows one wave-wide 16-byte-per-lane load fills
     constexpr int kBM = 32 * NW;                  // queries per workgroup
-    constexpr int DPW = TILE * 2 / 1024 / NW;     // such loads per wave per tile
+    constexpr int NL = TILE * 2 / 1024;           // such loads per tile
+    constexpr int DPW = NL >= NW ? NL / NW : 1;   // loads per wave per tile
     constexpr int NKB = BN / 32;                  // 32-key blocks of S^T
     constexpr int NC4 = BN / 16;                  // 16-key chunks of P^T
     constexpr int NDB = D / 32;                   // 32-wide dimension blocks of O^T
     constexpr int NQC = D / 16;                   // 16-wide contraction chunks of Q K^T
-    static_assert(DPW * NW * RPI == BN, "tile rows must split evenly over the waves");
+    static_assert((NL >= NW && DPW * NW == NL) || (NL < NW && 2 * NL <= NW), "tile loads must split evenly");
+    static_assert(NL * RPI == BN, "tile rows");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform: keep it (and all that derives from it) in
+    // scalar registers
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 31, h = lane >> 5;
-    const int grp = w >> 2;  // waves w and w + 4 share a SIMD
+    const int grp = w / (NW / 2);  // wave w runs on SIMD w % 4
 
     // Workgroups are dealt to the 8 XCDs round robin; regroup them so the
     // query blocks of one (b, h) run on one XCD and share its L2 copy of K, V.
@@ -200,15 +209,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     auto dma = [&](const char* src, uint16_t* tile, bool is_v, int key0) {
         const char* g = src + (int64_t)key0 * 2 * D;
         const int nvalid = Sk - key0;  // >= 1 for every tile loaded
+        int L0 = w * DPW;              // first load of this wave
+        if constexpr (NL < NW) {
+            // fewer loads than waves: K by waves 0 .. NL - 1, V by waves
+            // NL .. 2 NL - 1
+            L0 = w - (is_v ? NL : 0);
+            if (L0 < 0 || L0 >= NL) return;
+        }
 #pragma unroll
         for (int j = 0; j < DPW; ++j) {
-            const int row = (w * DPW + j) * RPI + lane / NCH;
+            const int row = (L0 + j) * RPI + lane / NCH;
             const int phys = lane % NCH;
             const int chunk = phys ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
             // rows past the sequence end repeat the last valid row (its scores
             // are masked, its values meet P = 0)
             const int srow = row < nvalid ? row : nvalid - 1;
-            lds_dma16(g + srow * 2 * D + (chunk << 4), tile + (w * DPW + j) * 512);
+            lds_dma16(g + srow * 2 * D + (chunk << 4), tile + (L0 + j) * 512);
         }
     };
 
@@ -257,8 +273,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
     };
 
     f32x16_t sacc[NKB];
-    bf16x8_t pprev[NC4];
-    unsigned pw[NKB * 8];  // P of the current tile as 32-bit words (pairs of bf16), assembled into pprev
+    u32x4_t pprev[NC4];  // P^T operand: P of the current tile as 32-bit words (pairs of bf16)
     constexpr int NPAIR = NKB * 8;  // pairs of S^T values per lane
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     // P for one pair of S^T values: exponentials, rounding to bf16 (the pair
@@ -272,7 +287,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         const float p0 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j], c, -mu));
         const float p1 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j + 1], c, -mu));
         const bf16x2_t pv2 = {(__bf16)p0, (__bf16)p1};
-        pw[pp] = __builtin_bit_cast(unsigned, pv2);
+        pprev[pp / 4][pp % 4] = __builtin_bit_cast(unsigned, pv2);
         return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
     };
 
@@ -284,7 +299,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         constexpr bool DO_PV = decltype(pv_c)::value, DO_S = decltype(s_c)::value;
         constexpr int N0 = DO_PV ? NPV : 0;
         constexpr int N = N0 + (DO_S ? NS : 0);
-        constexpr int R = 4;
+        // four waves per SIMD leave room for a ring of two only
+        constexpr int R = NW == 8 ? 4 : 2;
         auto rd = [&](int j) -> bf16x8_t { return j < N0 ? vread(vt8, j) : kread(kt8, j - N0); };
         bf16x8_t op[R];
 #pragma unroll
@@ -294,7 +310,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
         for (int j = 0; j < N; ++j) {
             if (j + R - 1 < N) op[(j + R - 1) % R] = rd(j + R - 1);
             if (j < N0) {
-                oacc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], pprev[j / NDB], oacc[j % NDB], 0, 0, 0);
+                oacc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], __builtin_bit_cast(bf16x8_t, pprev[j / NDB]),
+                                                                        oacc[j % NDB], 0, 0, 0);
             } else {
                 const int i = j - N0, kb = i % NKB, cc = i / NKB;
                 if (cc == 0) {
@@ -359,9 +376,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_fwd_kernel(const uint16_t* __
             }
         }
         l += rs;
-#pragma unroll
-        for (int c4 = 0; c4 < NC4; ++c4)
-            pprev[c4] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * c4], pw[4 * c4 + 1], pw[4 * c4 + 2], pw[4 * c4 + 3]});
     };
 
     // ---- prologue: K(0), V(0), K(1); every wave computes its S(0) ----------
@@ -473,7 +487,7 @@ hipError_t launch_d(const AttnArgs& a, int nsplit, float* pm, float* pl, float* 
 hipError_t launch_any(const AttnArgs& a, int nsplit, float* pm, float* pl, float* pO)
 {
     if (a.D == 128) return launch_d<128, 64, 8>(a, nsplit, pm, pl, pO);
-    return launch_d<64, 128, 8>(a, nsplit, pm, pl, pO);
+    return launch_d<64, 64, 16>(a, nsplit, pm, pl, pO);
 }
 
 }  // namespace
