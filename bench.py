@@ -67,23 +67,32 @@ def measured_traffic(kernel: str, workload: str):
 
 
 MAIN_STAGES = ("softmax_f32", "softmax_bf16", "attn_nc", "attn_causal", "decode")
-EXTRA_STAGES = ("decode_fused", "softmax_long_f32", "attn_lowocc", "attn_lowocc_splitk")
+EXTRA_STAGES = ("decode_fused", "softmax_long_f32", "attn_lowocc", "attn_lowocc_splitk",
+                "softmax_f32_if_rise", "softmax_f32_l0_one", "softmax_f32_block1", "softmax_f32_block1_if_rise")
+# rescale-policy A/B on the fp32 softmax batch: (rescale policy, block)
+RESCALE_STAGES = {"softmax_f32_if_rise": (1, 8), "softmax_f32_l0_one": (2, 8), "softmax_f32_block1": (0, 1),
+                  "softmax_f32_block1_if_rise": (1, 1)}
 
 STAGE_KERNELS = {  # stage -> kernels (in launch order) that make up one launch: a substring of the kernel
     # name, or (substring, grid size in threads) where stages share a kernel
-    "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256>"],
-    "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256>"],
+    "softmax_f32": ["row_softmax_kernel<false, 256, 32, true, 8, 256, 0>"],
+    "softmax_bf16": ["row_softmax_kernel<true, 256, 32, true, 8, 256, 0>"],
+    "softmax_f32_if_rise": ["row_softmax_kernel<false, 256, 32, true, 8, 256, 1>"],
+    "softmax_f32_l0_one": ["row_softmax_kernel<false, 256, 32, true, 8, 256, 2>"],
+    "softmax_f32_block1": ["row_softmax_kernel<false, 256, 32, true, 1, 256, 0>"],
+    "softmax_f32_block1_if_rise": ["row_softmax_kernel<false, 256, 32, true, 1, 256, 1>"],
     "attn_nc": ["attn_fwd_kernel<64, 64, 16, true>"],
     "attn_causal": [("attn_fwd_kernel<128, 64, 8, true>", 2048 * 512)],
     "decode": ["decode_partial_kernel<128, 8>", "merge_kernel<true, true, true>"],
-    "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512>"],
+    "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512, 0>"],
     "decode_fused": ["decode_fused_kernel<128, 4, true>"],
     "attn_lowocc": [("attn_fwd_kernel<128, 64, 8, true>", 32 * 512)],
     "attn_lowocc_splitk": [("attn_fwd_kernel<128, 64, 8, true>", 512 * 512), "merge_kernel<false, true, true>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
                 "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax",
-                "decode_fused": "decode", "attn_lowocc": "attn_fwd", "attn_lowocc_splitk": "attn_fwd"}
+                "decode_fused": "decode", "attn_lowocc": "attn_fwd", "attn_lowocc_splitk": "attn_fwd",
+                **{n: "row_softmax" for n in RESCALE_STAGES}}
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, command: str):
@@ -153,8 +162,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stages",
-                    default="softmax_f32,softmax_bf16,attn_nc,attn_causal,decode,decode_fused,softmax_long_f32,"
-                            "attn_lowocc,attn_lowocc_splitk")
+                    default=",".join(MAIN_STAGES + EXTRA_STAGES))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -186,19 +194,30 @@ def main():
 
     S = {}  # stage -> dict(fn, units, kind)
     t0 = time.perf_counter()
-    if "softmax_f32" in stages or "softmax_bf16" in stages:
+    rescale_stages = [n for n in RESCALE_STAGES if n in stages]
+    if "softmax_f32" in stages or "softmax_bf16" in stages or rescale_stages:
         w = inputs.WORKLOADS["softmax_large"]
         R, C = w["rows"], w["cols"]
         for dt in ("f32", "bf16"):
             name = f"softmax_{dt}"
-            if name not in stages:
+            if name not in stages and not (dt == "f32" and rescale_stages):
                 continue
             x = inputs.logits(R, C, 30.0, 202 if dt == "f32" else 205, dt).to(dev)
             y = torch.empty_like(x)
             es = 4 if dt == "f32" else 2
-            S[name] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 2 * es,
-                           kind="hbm", kernel="row_softmax",
-                           workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
+            if name in stages:
+                S[name] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 2 * es,
+                               kind="hbm", kernel="row_softmax",
+                               workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
+            if dt == "f32":
+                # the same batch under the other rescale policies (same bits,
+                # different work per block) and at one logit per block
+                for n in rescale_stages:
+                    rs, blk = RESCALE_STAGES[n]
+                    pol = ("unconditional", "conditional (only when the maximum rose)", "l started at 1")[rs]
+                    S[n] = dict(fn=(lambda x=x, y=y, rs=rs, blk=blk: tea.row_softmax_variant(x, rs, out=y, block=blk)),
+                                units=R * C * 8, kind="hbm", kernel="row_softmax",
+                                workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block {blk}, rescale {pol}")
             log(f"inputs {name} ready ({time.perf_counter() - t0:.1f}s)")
     if "softmax_long_f32" in stages:
         w = inputs.WORKLOADS["softmax_long"]  # rows longer than 16384: the two-read streaming path

@@ -74,6 +74,31 @@ enum tea_dtype { TEA_F32 = 0, TEA_BF16 = 1 };
 int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, float* m_out,
                 float* l_out, void* stream);
 
+/* Rescale policies of row_softmax_variant (see there). */
+enum tea_rescale { TEA_RESCALE_ALWAYS = 0, TEA_RESCALE_IF_RISE = 1, TEA_RESCALE_L0_ONE = 2 };
+
+/*
+ * row_softmax_variant -- row_softmax with a choice of how each lane's running
+ * normaliser is put on a new scale when a block is folded in.  The pages set
+ * two good kernels against each other here ("Online Softmax"
+ * (metalworking), Recognition guide: metal-flash-attention multiplies by the
+ * correction exp(m - m') only when the maximum rose, MLX multiplies every
+ * time), and note that the attention tutorial starts the normaliser at 1
+ * instead of 0 ("Online softmax" (roadmapper), Initialise honestly).
+ *   rescale  TEA_RESCALE_ALWAYS: multiply every block (what row_softmax does);
+ *            TEA_RESCALE_IF_RISE: compute the correction and multiply only
+ *              when the maximum rose (a wave skips the work when no lane's
+ *              maximum rose);
+ *            TEA_RESCALE_L0_ONE: start each lane's normaliser at 1, removed
+ *              by the zero correction of its first non-empty block;
+ *            anything else: TEA_EINVAL.
+ * All three return the same bits in y, m_out and l_out (the correction is
+ * exactly 1 when the maximum stays, and exactly 0 against the -inf start).
+ * Other arguments, limits and errors as for row_softmax.
+ */
+int row_softmax_variant(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, int rescale,
+                        float* m_out, float* l_out, void* stream);
+
 /*
  * attn_fwd -- O = softmax(Q K^T * scale) V per (batch, head), streaming K and
  * V in tiles with the online softmax so no row of scores is stored ("The

@@ -61,6 +61,17 @@ def test_row_softmax_validation(lib):
     assert f(NULL, NULL, 0, 8, tea.TEA_F32, 8, NULL, NULL, NULL) == tea.TEA_OK           # no rows: no-op
 
 
+def test_row_softmax_variant_validation(lib):
+    f = lib.row_softmax_variant
+    for bad in (-1, 3, 7):
+        assert f(FAKE, FAKE, 4, 8, tea.TEA_F32, 8, bad, NULL, NULL, NULL) == tea.TEA_EINVAL  # unknown policy
+    for rs in (tea.TEA_RESCALE_ALWAYS, tea.TEA_RESCALE_IF_RISE, tea.TEA_RESCALE_L0_ONE):
+        assert f(NULL, NULL, 4, 8, tea.TEA_F32, 8, rs, NULL, NULL, NULL) == tea.TEA_EINVAL      # null x, y
+        assert f(FAKE, FAKE, 4, 8, tea.TEA_F32, 3, rs, NULL, NULL, NULL) == tea.TEA_EUNSUPPORTED  # block 3
+        assert f(ODD, FAKE, 4, 8, tea.TEA_F32, 8, rs, NULL, NULL, NULL) == tea.TEA_EINVAL       # misaligned
+        assert f(NULL, NULL, 0, 8, tea.TEA_F32, 8, rs, NULL, NULL, NULL) == tea.TEA_OK          # no rows
+
+
 def test_attn_fwd_validation(lib):
     f = lib.attn_fwd
     A = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)]

@@ -195,3 +195,55 @@ def test_large_config_full_size(dtype, scale):
     _compare(xs, y.cpu()[idx], m.cpu()[idx], l.cpu()[idx], 1e-5 if dtype == "f32" else 4e-3,
              f"65536x8192 {dtype} x{scale}")
     del x, y
+
+
+# ---- rescale policies: conditional (metal-flash-attention), unconditional
+# (MLX) and the tutorial's l = 1 start give the same bits -------------------
+
+def _bits(t):
+    t = t.contiguous()
+    return to_np(t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16))
+
+
+def _shaped_rows(rows, cols, dtype, seed):
+    """N(0,1) x 30 rows, plus rows that make every branch of the fold run:
+    a rising ramp (the maximum rises in every block), a falling ramp (it never
+    rises after the first block), a -inf row, a row -inf in its first half,
+    and one large jump at the end."""
+    x = inputs.logits(rows, cols, 30.0, seed, "f32")
+    ramp = torch.arange(cols, dtype=torch.float32) * 0.01
+    x[0] = ramp
+    x[1] = -ramp
+    x[2] = -math.inf
+    x[3, : cols // 2] = -math.inf
+    x[4, -1] = 1.0e4
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("rescale", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cols,block", [(1, 8), (63, 1), (1000, 8), (8192, 1), (8192, 8), (8192, 32), (12345, 4),
+                                        (20000, 8), (65536, 2)])
+def test_rescale_variants_bitwise_equal(rescale, dtype, cols, block):
+    say(f"row_softmax_variant rescale={rescale} {dtype} cols={cols} block={block}")
+    rows = 24
+    x = _shaped_rows(rows, cols, dtype, 300 + cols).to(DEV)
+    y0, m0, l0 = tea.row_softmax(x, block=block, stats=True)
+    y1, m1, l1 = tea.row_softmax_variant(x, rescale, block=block, stats=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y0), _bits(y1)), "outputs differ"
+    assert np.array_equal(_bits(m0), _bits(m1)), "row maxima differ"
+    assert np.array_equal(_bits(l0), _bits(l1)), "normalisers differ"
+
+
+def test_rescale_variants_match_oracle_and_in_place():
+    say("row_softmax_variant in place, against the oracle")
+    x_cpu = _shaped_rows(16, 1024, "f32", 77)
+    ref, mref, lref = oracle.softmax_rows(x_cpu.numpy())
+    for rescale in (tea.TEA_RESCALE_ALWAYS, tea.TEA_RESCALE_IF_RISE, tea.TEA_RESCALE_L0_ONE):
+        x = x_cpu.to(DEV)
+        y, m, l = tea.row_softmax_variant(x, rescale, out=x, stats=True)
+        torch.cuda.synchronize()
+        check_softmax(to_np(y), ref, 1e-5, f"rescale={rescale}")
+        assert np.array_equal(to_np(m).astype(np.float64), mref)
+        assert to_np(l)[2] == 0.0 and np.all(to_np(y)[2] == 0.0)

@@ -24,13 +24,14 @@ __all__ = [
 
 TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED, TEA_EHIP = 0, 1, 2, 3
 TEA_F32, TEA_BF16 = 0, 1
+TEA_RESCALE_ALWAYS, TEA_RESCALE_IF_RISE, TEA_RESCALE_L0_ONE = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtea.so")
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ("row_softmax", "attn_fwd", "attn_fwd_splitk_workspace_bytes", "attn_fwd_splitk",
+EXPORTS = ("row_softmax", "row_softmax_variant", "attn_fwd", "attn_fwd_splitk_workspace_bytes", "attn_fwd_splitk",
            "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_fused",
            "merge_partials",
            "tea_status_string", "tea_abi_version")
@@ -59,6 +60,8 @@ def load_library():
             P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
             lib.row_softmax.argtypes = [P, P, I64, I64, I, I, P, P, P]
             lib.row_softmax.restype = I
+            lib.row_softmax_variant.argtypes = [P, P, I64, I64, I, I, I, P, P, P]
+            lib.row_softmax_variant.restype = I
             lib.attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, F, I, I, P, P]
             lib.attn_fwd.restype = I
             lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -119,6 +122,24 @@ def row_softmax(x: torch.Tensor, out: torch.Tensor | None = None, block: int = 8
     l = torch.empty(rows, dtype=torch.float32, device=x.device) if stats else None
     _check("row_softmax", load_library().row_softmax(_ptr(x), _ptr(y), rows, cols, _dcode(x.dtype), int(block),
                                                      _ptr(m), _ptr(l), _stream(x)))
+    return (y, m, l) if stats else y
+
+
+def row_softmax_variant(x: torch.Tensor, rescale: int, out: torch.Tensor | None = None, block: int = 8,
+                        stats: bool = False):
+    """row_softmax with the rescale policy of the online fold chosen:
+    TEA_RESCALE_ALWAYS, TEA_RESCALE_IF_RISE or TEA_RESCALE_L0_ONE (same bits
+    as row_softmax for every policy)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    y = torch.empty_like(x) if out is None else out
+    _dev(x, y)
+    rows, cols = x.shape
+    m = torch.empty(rows, dtype=torch.float32, device=x.device) if stats else None
+    l = torch.empty(rows, dtype=torch.float32, device=x.device) if stats else None
+    _check("row_softmax_variant", load_library().row_softmax_variant(_ptr(x), _ptr(y), rows, cols, _dcode(x.dtype),
+                                                                     int(block), int(rescale), _ptr(m), _ptr(l),
+                                                                     _stream(x)))
     return (y, m, l) if stats else y
 
 

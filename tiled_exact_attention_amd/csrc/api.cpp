@@ -38,9 +38,11 @@ const char* tea_status_string(int status)
     }
 }
 
-int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, float* m_out,
-                float* l_out, void* stream)
+int row_softmax_variant(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, int rescale,
+                        float* m_out, float* l_out, void* stream)
 {
+    if (rescale != TEA_RESCALE_ALWAYS && rescale != TEA_RESCALE_IF_RISE && rescale != TEA_RESCALE_L0_ONE)
+        return TEA_EINVAL;
     if (rows < 0 || cols < 0) return TEA_EINVAL;
     if (dtype != TEA_F32 && dtype != TEA_BF16) return TEA_EINVAL;
     if (block < 0) return TEA_EINVAL;
@@ -59,7 +61,16 @@ int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, i
     }
     if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4))) return TEA_EINVAL;
     tea::RowSoftmaxArgs a{x, y, rows, cols, dtype == TEA_BF16, block, m_out, l_out, (hipStream_t)stream};
+    a.rescale = rescale == TEA_RESCALE_IF_RISE ? tea::kRescaleIfRise
+                : rescale == TEA_RESCALE_L0_ONE ? tea::kRescaleL0One
+                                                : tea::kRescaleAlways;
     return status_of(tea::launch_row_softmax(a));
+}
+
+int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, float* m_out,
+                float* l_out, void* stream)
+{
+    return row_softmax_variant(x, y, rows, cols, dtype, block, TEA_RESCALE_ALWAYS, m_out, l_out, stream);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq, int Sk, int D,

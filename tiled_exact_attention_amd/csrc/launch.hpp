@@ -8,6 +8,9 @@
 
 namespace tea {
 
+// rescale policy of the online fold (the three give the same bits)
+enum : int { kRescaleAlways = 0, kRescaleIfRise = 1, kRescaleL0One = 2 };
+
 struct RowSoftmaxArgs {
     const void* x;
     void* y;
@@ -17,6 +20,7 @@ struct RowSoftmaxArgs {
     float* m_out;
     float* l_out;
     hipStream_t stream;
+    int rescale = kRescaleAlways;
 };
 hipError_t launch_row_softmax(const RowSoftmaxArgs& a);
 int64_t row_softmax_max_cols();

@@ -23,7 +23,41 @@
 
 namespace tea {
 
-template <bool BF16, int TPR, int N, bool VEC, int BLOCK, int WG>
+// One step of the per-lane fold: the state (m, l) absorbs a block of B
+// logits.  RS picks how the accumulated l is put on the new scale; all three
+// give the same bits:
+//   kRescaleAlways  multiply by c = exp(m - m') every block, as the MLX kernel
+//                   does ("Online Softmax" (metalworking), Recognition guide);
+//   kRescaleIfRise  compute c and multiply only when the maximum rose, the
+//                   guard of metal-flash-attention (same passage).  Lanes run
+//                   in lock step, so the work is skipped when no lane of the
+//                   wave saw a rise; for a lane without a rise c is exactly
+//                   exp2(0) = 1 and fma(l, 1, s) = l + s;
+//   kRescaleL0One   start from l = 1 instead of 0, as the attention tutorial
+//                   does ("Online softmax" (roadmapper), Initialise honestly):
+//                   the first non-empty block has c = exp(-inf) = 0, which
+//                   removes the 1 (fma(1, 0, s) = s).
+template <int RS, int B>
+__device__ __forceinline__ void fold_block(const float* x, float& m, float& l)
+{
+    float bm = x[0];
+#pragma unroll
+    for (int e = 1; e < B; ++e) bm = fmaxf(bm, x[e]);
+    const float mn = fmaxf(m, bm);
+    const float mu = guard_max(mn);
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < B; ++e) s += exp2_hw((x[e] - mu) * kLog2eHi);
+    if constexpr (RS == kRescaleIfRise) {
+        if (__builtin_amdgcn_ballot_w64(mn > m)) l = fmaf(l, exp2_hw((m - mu) * kLog2eHi), s);
+        else l = l + s;
+    } else {
+        l = fmaf(l, exp2_hw((m - mu) * kLog2eHi), s);  // c = 0 on the first non-empty block
+    }
+    m = mn;
+}
+
+template <bool BF16, int TPR, int N, bool VEC, int BLOCK, int WG, int RS>
 __global__ __launch_bounds__(WG) void row_softmax_kernel(const void* xv, void* yv, int64_t rows, int64_t cols,
                                                          float* __restrict__ m_out, float* __restrict__ l_out)
 {
@@ -89,21 +123,9 @@ __global__ __launch_bounds__(WG) void row_softmax_kernel(const void* xv, void* y
     }
 
     // ---- a2: per-lane online fold in blocks of BLOCK -----------------------
-    float m = kNegInf, l = 0.0f;
+    float m = kNegInf, l = RS == kRescaleL0One ? 1.0f : 0.0f;
 #pragma unroll
-    for (int b0 = 0; b0 < N; b0 += BLOCK) {
-        float bm = x[b0];
-#pragma unroll
-        for (int e = 1; e < BLOCK; ++e) bm = fmaxf(bm, x[b0 + e]);
-        const float mn = fmaxf(m, bm);
-        const float mu = guard_max(mn);
-        const float c = exp2_hw((m - mu) * kLog2eHi);  // 0 on the first non-empty block
-        float s = 0.0f;
-#pragma unroll
-        for (int e = 0; e < BLOCK; ++e) s += exp2_hw((x[b0 + e] - mu) * kLog2eHi);
-        l = fmaf(l, c, s);
-        m = mn;
-    }
+    for (int b0 = 0; b0 < N; b0 += BLOCK) fold_block<RS, BLOCK>(x + b0, m, l);
 
     // ---- a3: merge the lanes' states ---------------------------------------
     float M = wave_reduce(m, MaxOp());
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(WG) void row_softmax_kernel(const void* xv, void* y
 // logits) per step in blocks of BLOCK with the recurrence above, and the
 // lanes' states are merged as above; pass 2 streams the row again and writes
 // y = exp(x - M) / L.
-template <bool BF16, bool VEC, int BLOCK, int WG>
+template <bool BF16, bool VEC, int BLOCK, int WG, int RS>
 __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, void* yv, int64_t cols,
                                                                 float* __restrict__ m_out, float* __restrict__ l_out)
 {
@@ -237,25 +259,13 @@ __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, 
     };
 
     // ---- pass 1: fold -------------------------------------------------------
-    float m = kNegInf, l = 0.0f;
+    float m = kNegInf, l = RS == kRescaleL0One ? 1.0f : 0.0f;
     for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)UN * WG) {
         float x[N];
 #pragma unroll
         for (int u = 0; u < UN; ++u) load(v0 + (int64_t)u * WG + t, x + u * W);
 #pragma unroll
-        for (int b0 = 0; b0 < N; b0 += B) {
-            float bm = x[b0];
-#pragma unroll
-            for (int e = 1; e < B; ++e) bm = fmaxf(bm, x[b0 + e]);
-            const float mn = fmaxf(m, bm);
-            const float mu = guard_max(mn);
-            const float c = exp2_hw((m - mu) * kLog2eHi);
-            float s = 0.0f;
-#pragma unroll
-            for (int e = 0; e < B; ++e) s += exp2_hw((x[b0 + e] - mu) * kLog2eHi);
-            l = fmaf(l, c, s);
-            m = mn;
-        }
+        for (int b0 = 0; b0 < N; b0 += B) fold_block<RS, B>(x + b0, m, l);
     }
     // ---- merge the lanes' states -------------------------------------------
     float M = wave_reduce(m, MaxOp());
@@ -341,81 +351,76 @@ namespace {
 // longest row held in registers (one workgroup of 512 lanes x 32 logits)
 constexpr int64_t kRegisterCols = 16384;
 
-template <bool BF16, bool VEC, int TPR, int N, int BLOCK>
+template <bool BF16, bool VEC, int RS, int TPR, int N, int BLOCK>
 hipError_t launch_one(const RowSoftmaxArgs& a)
 {
     constexpr int WG = TPR > 256 ? TPR : 256;
     constexpr int RPW = WG / TPR;
     const int64_t grid = (a.rows + RPW - 1) / RPW;
-    hipLaunchKernelGGL((row_softmax_kernel<BF16, TPR, N, VEC, BLOCK, WG>), dim3((unsigned)grid), dim3(WG), 0,
+    hipLaunchKernelGGL((row_softmax_kernel<BF16, TPR, N, VEC, BLOCK, WG, RS>), dim3((unsigned)grid), dim3(WG), 0,
                        a.stream, a.x, a.y, a.rows, a.cols, a.m_out, a.l_out);
     return hipGetLastError();
 }
 
-template <bool BF16, bool VEC, int TPR, int N>
+template <bool BF16, bool VEC, int RS, int TPR, int N>
 hipError_t launch_blocks(const RowSoftmaxArgs& a)
 {
     const int b = a.block < N ? a.block : N;
     switch (b) {
-    case 1: return launch_one<BF16, VEC, TPR, N, 1>(a);
-    case 2: return launch_one<BF16, VEC, TPR, N, 2>(a);
-    case 4: return launch_one<BF16, VEC, TPR, N, 4>(a);
-    case 8: return launch_one<BF16, VEC, TPR, N, (8 < N ? 8 : N)>(a);
-    case 16: return launch_one<BF16, VEC, TPR, N, (16 < N ? 16 : N)>(a);
-    default: return launch_one<BF16, VEC, TPR, N, (32 < N ? 32 : N)>(a);
+    case 1: return launch_one<BF16, VEC, RS, TPR, N, 1>(a);
+    case 2: return launch_one<BF16, VEC, RS, TPR, N, 2>(a);
+    case 4: return launch_one<BF16, VEC, RS, TPR, N, 4>(a);
+    case 8: return launch_one<BF16, VEC, RS, TPR, N, (8 < N ? 8 : N)>(a);
+    case 16: return launch_one<BF16, VEC, RS, TPR, N, (16 < N ? 16 : N)>(a);
+    default: return launch_one<BF16, VEC, RS, TPR, N, (32 < N ? 32 : N)>(a);
     }
 }
 
-template <bool BF16, bool VEC>
-hipError_t launch_stream(const RowSoftmaxArgs& a)
+template <bool BF16, bool VEC, int RS, int BLOCK>
+hipError_t launch_stream_one(const RowSoftmaxArgs& a)
 {
     constexpr int WG = 512;
-    const dim3 grid((unsigned)a.rows), blk(WG);
-    switch (a.block) {
-    case 1:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 1, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    case 2:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 2, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    case 4:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 4, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    case 8:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 8, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    case 16:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 16, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    default:
-        hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, 32, WG>), grid, blk, 0, a.stream, a.x, a.y, a.cols,
-                           a.m_out, a.l_out);
-        break;
-    }
+    hipLaunchKernelGGL((row_softmax_stream_kernel<BF16, VEC, BLOCK, WG, RS>), dim3((unsigned)a.rows), dim3(WG), 0,
+                       a.stream, a.x, a.y, a.cols, a.m_out, a.l_out);
     return hipGetLastError();
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int RS>
+hipError_t launch_stream(const RowSoftmaxArgs& a)
+{
+    switch (a.block) {
+    case 1: return launch_stream_one<BF16, VEC, RS, 1>(a);
+    case 2: return launch_stream_one<BF16, VEC, RS, 2>(a);
+    case 4: return launch_stream_one<BF16, VEC, RS, 4>(a);
+    case 8: return launch_stream_one<BF16, VEC, RS, 8>(a);
+    case 16: return launch_stream_one<BF16, VEC, RS, 16>(a);
+    default: return launch_stream_one<BF16, VEC, RS, 32>(a);
+    }
+}
+
+template <bool BF16, bool VEC, int RS>
 hipError_t launch_cols(const RowSoftmaxArgs& a)
 {
-    if (a.cols > kRegisterCols) return launch_stream<BF16, VEC>(a);
+    if (a.cols > kRegisterCols) return launch_stream<BF16, VEC, RS>(a);
     // Smallest per-lane register count that covers the row: one wave per row
     // up to 2048 logits, one workgroup of 4 (or 8) waves beyond.
     const int64_t c = a.cols;
     if constexpr (!BF16) {
-        if (c <= 256) return launch_blocks<BF16, VEC, 64, 4>(a);
+        if (c <= 256) return launch_blocks<BF16, VEC, RS, 64, 4>(a);
     }
-    if (c <= 512) return launch_blocks<BF16, VEC, 64, 8>(a);
-    if (c <= 1024) return launch_blocks<BF16, VEC, 64, 16>(a);
-    if (c <= 2048) return launch_blocks<BF16, VEC, 64, 32>(a);
-    if (c <= 4096) return launch_blocks<BF16, VEC, 256, 16>(a);
-    if (c <= 8192) return launch_blocks<BF16, VEC, 256, 32>(a);
-    return launch_blocks<BF16, VEC, 512, 32>(a);
+    if (c <= 512) return launch_blocks<BF16, VEC, RS, 64, 8>(a);
+    if (c <= 1024) return launch_blocks<BF16, VEC, RS, 64, 16>(a);
+    if (c <= 2048) return launch_blocks<BF16, VEC, RS, 64, 32>(a);
+    if (c <= 4096) return launch_blocks<BF16, VEC, RS, 256, 16>(a);
+    if (c <= 8192) return launch_blocks<BF16, VEC, RS, 256, 32>(a);
+    return launch_blocks<BF16, VEC, RS, 512, 32>(a);
+}
+
+template <int RS>
+hipError_t launch_rs(const RowSoftmaxArgs& a, bool vec)
+{
+    if (a.bf16) return vec ? launch_cols<true, true, RS>(a) : launch_cols<true, false, RS>(a);
+    return vec ? launch_cols<false, true, RS>(a) : launch_cols<false, false, RS>(a);
 }
 
 }  // namespace
@@ -431,8 +436,9 @@ hipError_t launch_row_softmax(const RowSoftmaxArgs& a)
     }
     const int W = a.bf16 ? 8 : 4;
     const bool vec = (a.cols % W == 0) && ((uintptr_t)a.x % 16 == 0) && ((uintptr_t)a.y % 16 == 0);
-    if (a.bf16) return vec ? launch_cols<true, true>(a) : launch_cols<true, false>(a);
-    return vec ? launch_cols<false, true>(a) : launch_cols<false, false>(a);
+    if (a.rescale == kRescaleIfRise) return launch_rs<kRescaleIfRise>(a, vec);
+    if (a.rescale == kRescaleL0One) return launch_rs<kRescaleL0One>(a, vec);
+    return launch_rs<kRescaleAlways>(a, vec);
 }
 
 int64_t row_softmax_max_cols() { return INT64_MAX; }
