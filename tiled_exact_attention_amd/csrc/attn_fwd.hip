@@ -87,15 +87,15 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
 // per SIMD).
 //
 // Two groups of NW / 2 waves per workgroup, NW / 8 waves of each group on
-// every SIMD, take turns ("ping-pong"): while one group runs the matrix phase of a
-// tile (M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, MFMAs fed from LDS)
-// the other runs the softmax phase (X: row maximum, reference, exponentials,
-// P), which is vector work only.  A SIMD then overlaps one group's MFMAs with
-// the other group's vector instructions; with 16 waves two waves of a group
-// share a SIMD, which doubles the vector issue rate of the softmax phase (a
-// single wave issues a vector instruction only every few cycles).  Each wave alternates X(t), M(t),
-// X(t+1), ...; group 1 runs one phase behind group 0, and every phase ends
-// at a workgroup barrier:
+// every SIMD, take turns ("ping-pong"): while one group runs the matrix
+// phase of a tile (M: O += V(t)^T P(t) and S(t+1) = K(t+1) Q^T, MFMAs fed
+// from LDS) the other runs the softmax phase (X: reference, exponentials,
+// P), which is vector work only.  A SIMD then overlaps one group's MFMAs
+// with the other group's vector instructions; with 16 waves two waves of a
+// group share a SIMD, which raises the vector issue rate of the softmax
+// phase (a single wave issues a vector instruction only every few cycles).
+// Each wave alternates X(t), M(t), X(t+1), ...; group 1 runs one phase
+// behind group 0, and every phase ends at a workgroup barrier:
 //   slot 2t  : group 0 X(t)        group 1 M(t-1)
 //   slot 2t+1: group 0 M(t)        group 1 X(t)      + loads of V(t+1), K(t+2)
 // M(t) reads V(t) and K(t+1) (slots 2t+1 and 2t+2); the loads issued in slot
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // causal is a runtime flag: as a template parameter it made hipcc spill
     // the non-causal instantiation
     const bool CAUSAL = causal != 0;
-    constexpr int TILE = BN * D;                  // elements per K or V tile (16 KiB)
+    constexpr int TILE = BN * D;                  // elements per K or V tile (16 KiB at D = 128, 8 KiB at 64)
     constexpr int NCH = D / 8;                    // 16-byte chunks per row
     constexpr int RPI = 1024 / (2 * D);           // rows one wave-wide 16-byte-per-lane load fills
     constexpr int kBM = 32 * NW;                  // queries per workgroup
