@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stages",
                     default=",".join(MAIN_STAGES + EXTRA_STAGES))
+    ap.add_argument("--no-box-references", action="store_true",
+                    help="skip the copy, read and GEMM rates of this box (secondary fractions)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -207,7 +209,7 @@ def main():
             es = 4 if dt == "f32" else 2
             if name in stages:
                 S[name] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 2 * es,
-                               kind="hbm", kernel="row_softmax",
+                               kind="hbm", kernel="row_softmax", wfrac=0.5,
                                workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
             if dt == "f32":
                 # the same batch under the other rescale policies (same bits,
@@ -216,7 +218,7 @@ def main():
                     rs, blk = RESCALE_STAGES[n]
                     pol = ("unconditional", "conditional (only when the maximum rose)", "l started at 1")[rs]
                     S[n] = dict(fn=(lambda x=x, y=y, rs=rs, blk=blk: tea.row_softmax_variant(x, rs, out=y, block=blk)),
-                                units=R * C * 8, kind="hbm", kernel="row_softmax",
+                                units=R * C * 8, kind="hbm", kernel="row_softmax", wfrac=0.5,
                                 workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block {blk}, rescale {pol}")
             log(f"inputs {name} ready ({time.perf_counter() - t0:.1f}s)")
     if "softmax_long_f32" in stages:
@@ -225,7 +227,7 @@ def main():
         x = inputs.logits(R, C, 30.0, 206, "f32").to(dev)
         y = torch.empty_like(x)
         S["softmax_long_f32"] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 12,
-                                     kind="hbm", kernel="row_softmax",
+                                     kind="hbm", kernel="row_softmax", wfrac=1 / 3,
                                      workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block 8, two reads + one write")
         log(f"inputs softmax_long_f32 ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_nc" in stages:
@@ -274,12 +276,14 @@ def main():
                                tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=ns, workspace=ws,
                                                                out=od)),
                            units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode",
+                           wfrac=B * H * D * 2 / (tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4),
                            workload=f"decode B{B} H{H} Lmax{Lmax} D{D} bf16 splits{ns} sum(kv_len)={tot}")
         if "decode_fused" in stages:
             of = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
             S["decode_fused"] = dict(fn=(lambda qd=qd, Kd=Kd, Vd=Vd, kvd=kvd, ns=ns, of=of:
                                          tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=ns, out=of)),
                                      units=S["decode"]["units"], kind="hbm", kernel="decode",
+                                     wfrac=S["decode"]["wfrac"],
                                      workload=S["decode"]["workload"] + ", one launch")
         if "decode" not in stages:
             del S["decode"]
@@ -350,6 +354,11 @@ def main():
         times[n] = [a.elapsed_time(b) for a, b in ev]
         log(f"extra stage {n}: {k} warm-up and {args.steps} timed calls")
 
+    box = None if (args.calibrate_copy or args.no_box_references) else box_references(dev, stream)
+    if box:
+        log(f"box references: copy {box['copy_GBps']:.0f} GB/s, read {box['read_GBps']:.0f} GB/s, "
+            f"bf16 GEMM {box['gemm_bf16_TFLOPs']:.0f} TFLOP/s")
+
     paths = {}
     for n in names + extras:
         t = times[n]
@@ -369,6 +378,16 @@ def main():
                          "frac": round(ach / peak, 4), "traffic": measured_traffic(s["kernel"], n),
                          "algorithmic_units_per_launch": s["units"]},
         }
+        if box:
+            if s["kind"] == "hbm":
+                # what this box's copy and read kernels would take for the
+                # same bytes: the written bytes and as many read ones as a
+                # copy, the remaining reads as a pure read
+                f = s["wfrac"]
+                t_box = 2 * f / box["copy_GBps"] + (1 - 2 * f) / box["read_GBps"]
+                paths[n]["frac_of_box"] = round(ach * t_box, 4)
+            else:
+                paths[n]["frac_of_box"] = round(ach / box["gemm_bf16_TFLOPs"], 4)
 
     head = "softmax_f32" if "softmax_f32" in paths else names[0]
     hp = paths[head]
@@ -390,12 +409,54 @@ def main():
         "roofline": hp["roofline"],
         "paths": paths,
     }
+    if box:
+        out["box_references"] = box
     if "attn_causal" in paths:
         out["attention_tflops"] = paths["attn_causal"]["roofline"]["achieved"]
 
     if not args.no_cpu_baseline and "softmax_f32" in S:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def box_references(dev, stream):
+    """Rates this box reaches with plain library kernels, for secondary
+    fractions: a 1 GiB device copy (bytes read + written), a 1 GiB fp32 sum
+    (bytes read) and an 8192^3 bf16 GEMM (torch.mm, contiguous operands)."""
+    import numpy as np
+    import torch
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e-3
+
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    t_copy = timed(lambda: y.copy_(x), 10)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    t_read = timed(lambda: torch.sum(x, 0, out=acc), 10)
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    t_gemm = timed(lambda: torch.mm(a, b, out=c), 10)
+    del a, b, c
+    return {"copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1), "read_GBps": round((1 << 30) / t_read / 1e9, 1),
+            "gemm_bf16_TFLOPs": round(2 * n ** 3 / t_gemm / 1e12, 1),
+            "how": "device copy of 1 GiB (read + write bytes), fp32 sum of 1 GiB (read bytes), torch.mm bf16 "
+                   "8192^3; medians of 10; frac_of_box = achieved / the rate these give for the same bytes or flops"}
 
 
 def cpu_baseline(budget_s: float):
