@@ -162,8 +162,17 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     const int split = logical % nsplit;
     const int lq_block = logical / nsplit;
     int qb = lq_block % nqb;
-    const int64_t bh = lq_block / nqb;
+    int64_t bh = lq_block / nqb;
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+    const int nbh = G / (nqb * nsplit);
+    if (CAUSAL && nsplit == 1 && G % 8 == 0 && nbh % 8 == 0) {
+        // each XCD owns nbh / 8 heads and takes their query blocks longest
+        // first across its heads: every head's longest block, then every
+        // head's next longest, ...
+        const int x = bid % 8, local = bid / 8, bhx = nbh / 8;
+        qb = nqb - 1 - local / bhx;
+        bh = (int64_t)x * bhx + local % bhx;
+    }
     const int q0 = qb * kBM;
     const int qrow = q0 + w * 32 + lq;
     const int qlast = q0 + w * 32 + 31;  // last query of this wave
