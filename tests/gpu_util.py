@@ -12,7 +12,6 @@ preserved):
     |ref| >= 4 a bf16 output alone can be off by half an ulp (>= 2^-6), so
     those entries are held to half a bf16 ulp of ref plus 2e-3.
 """
-import math
 import os
 import sys
 
