@@ -6,8 +6,9 @@ preserved):
   - fp32 softmax: elementwise relative error <= 1e-5 where the reference is a
     normal fp32 number (>= 2^-126); below that, absolute error <= 2^-126
     (flush to zero accepted).  Outputs finite and in [0, 1].
-  - bf16 softmax: elementwise relative <= 4e-3 (bf16 rounding is at most
-    2^-9 = 1.95e-3 relative, plus the fp32 computation), same floor.
+  - bf16 softmax: elementwise relative <= 4e-3 (bf16 keeps 8 significant
+    bits, so rounding to nearest is at most 2^-8 = 3.91e-3 relative, plus the
+    fp32 computation), same floor.
   - attention / decode: max abs error <= 1e-2 against the fp64 oracle; where
     |ref| >= 4 a bf16 output alone can be off by half an ulp (>= 2^-6), so
     those entries are held to half a bf16 ulp of ref plus 2e-3.

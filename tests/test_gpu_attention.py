@@ -1,10 +1,11 @@
 """GPU parity of attn_fwd against the fp64 oracle (attention from its
 definition).
 
-The log-sum-exp output is m + ln(l) with l summed from the same bf16-rounded
-weights that multiply V (so that it stays consistent with O for a merge of
-partial outputs); rounding each weight moves l by at most 2^-9 relative, so
-ln(l) by at most log(1 + 2^-9) < 1.96e-3: the tolerance is 2.5e-3.
+The log-sum-exp output is m + ln(l).  At D = 64 l sums the same bf16-rounded
+weights that multiply V, at D = 128 the fp32 weights before rounding.  bf16
+keeps 8 significant bits, so rounding a weight to nearest moves it by at most
+2^-8 relative, l by as much and ln(l) by at most -ln(1 - 2^-8) < 3.92e-3: the
+tolerance is 4e-3.
 
 Workloads: non-causal B4 H16 S2048 D64 and causal B2 H32 S8192 D128, bf16
 N(0,1), scale 1/sqrt(D), at full size on sampled query rows; small shapes in
@@ -26,7 +27,7 @@ from gpu_util import check_attention, half_ulp_bf16, say, to_np
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-LSE_TOL = 2.5e-3
+LSE_TOL = 4e-3
 
 
 def _np32(t):
@@ -66,14 +67,14 @@ def test_noncausal_rectangular(Sq, Sk):
 
 def test_fp32_output():
     """With an fp32 output the error left is P's rounding to bf16 before the
-    P V product (2^-9 relative per weight), so at most 2^-9 * max|v| per
+    P V product (2^-8 relative per weight), so at most 2^-8 * max|v| per
     entry; every entry is checked against that bound."""
     say("attn_fwd fp32 output")
     q, k, v = inputs.qkv(1, 2, 500, 500, 128, seed=3)
     o, _, scale = _run(q, k, v, True, out_dtype=torch.float32)
     O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), scale, True)
     err = np.abs(to_np(o) - O)
-    bound = 2.0 ** -9 * np.abs(_np32(v)).max() + 1e-5
+    bound = 2.0 ** -8 * np.abs(_np32(v)).max() + 1e-5
     assert np.max(err) <= bound, f"fp32-output max abs err {np.max(err):.2e} > {bound:.2e}"
     print(f"fp32-output max abs err {np.max(err):.2e} (bound {bound:.2e})")
 
@@ -87,10 +88,15 @@ def test_closed_forms():
     # causal row 0 sees key 0 only
     o, _, _ = _run(q, k, v, True)
     assert torch.equal(o.cpu()[:, :, 0], v[:, :, 0])
-    # constant V: constant O (bf16 1.5 is exact)
+    # constant V: constant O (bf16 1.5 is exact); at D = 64 l sums the same
+    # rounded weights as the numerator, at D = 128 the unrounded ones, which
+    # leaves the weights' rounding (2^-8 relative)
     vc = torch.full_like(v, 1.5)
     o, _, _ = _run(q, k, vc, True, out_dtype=torch.float32)
     assert float((o - 1.5).abs().max()) <= 1e-5
+    q2, k2, _ = inputs.qkv(2, 2, 200, 200, 128, seed=5)
+    o, _, _ = _run(q2, k2, torch.full_like(q2, 1.5), True, out_dtype=torch.float32)
+    assert float((o - 1.5).abs().max()) <= 1.5 * 2.0 ** -8 + 1e-5
     # large scale: logits far apart, no overflow or NaN
     o, lse, _ = _run(q, k, v, False, scale=30.0)
     O, _ = oracle.attention(_np32(q), _np32(k), _np32(v), 30.0, False)
@@ -111,14 +117,25 @@ def _ramp_inputs(B, H, Sq, Sk, D, slope, seed):
     return q.contiguous(), k.contiguous(), v
 
 
-@pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("causal", [False, True])
 def _p_rounding_bound(q, k, v, scale, causal, O, L):
-    """Bound on what rounding the weights to bf16 does to O.  With
-    p~_j = p_j (1 + d_j), |d_j| <= 2^-9, and l summed from the same p~, the
-    output is the convex combination sum_j w~_j v_j with
+    """Bound on what rounding the weights to bf16 does to O, with
+    p~_j = p_j (1 + d_j), |d_j| <= 2^-8 (bf16 keeps 8 significant bits).
+    At D = 64 l sums the same p~, and
+    the output is the convex combination sum_j w~_j v_j with
     w~_j = w_j (1 + d_j) / (1 + sum_i w_i d_i), so
-    |O~ - O| <= 2^-8 / (1 - 2^-9) * sum_j w_j |v_j - O|, per row and dim.
+    |O~ - O| <= 2^-7 / (1 - 2^-8) * sum_j w_j |v_j - O|, per row and dim.
+    At D = 128 l sums the unrounded p, so O~ = sum_j w_j (1 + d_j) v_j and
+    |O~ - O| <= 2^-8 * sum_j w_j |v_j|.
+    The scores carry errors of their own: an fp32 dot product of D bf16
+    products is within D 2^-24 g_j of the exact one (g_j = scale sum_i
+    |q_i k_ji|), and the exponent s c - mu (c = scale log2 e, mu the row's
+    reference, at most the row's largest |s| c plus the lag) is rounded once
+    more, within 2^-24 (|s_j| + max_i |s_i| + 6) / ln 2 in base-two units,
+    i.e. 2^-24 (g_j + max_i g_i + 6) in the weight's logarithm; the
+    exponential adds a few ulps (2^-21).  An error e_j in weight j's
+    logarithm moves O, to first order, by sum_j w_j e_j (v_j - O), so at
+    most sum_j w_j |e_j| (|v_j| + |O|); that term is added with 1% for the
+    second order.
     The weights w_j = exp(s_j - L) come from the oracle's L (fp64)."""
     qf, kf, vf = (np.asarray(t, np.float64) for t in (q, k, v))
     out = np.empty_like(O)
@@ -129,9 +146,17 @@ def _p_rounding_bound(q, k, v, scale, causal, O, L):
         if causal:
             s = np.where(np.arange(Sk)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
         w = np.exp(s - L[:, :, r0:r1, None])
-        dev = np.abs(vf[:, :, None, :, :] - O[:, :, r0:r1, None, :])  # [b, h, q, k, d]
-        out[:, :, r0:r1] = np.einsum("bhqk,bhqkd->bhqd", w, dev)
-    return out * (2.0 ** -8 / (1.0 - 2.0 ** -9))
+        g = np.einsum("bhqd,bhkd->bhqk", np.abs(qf[:, :, r0:r1]), np.abs(kf)) * scale
+        e = 2.0 ** -24 * ((qf.shape[-1] + 1) * g + g.max(axis=-1, keepdims=True) + 6.0) + 2.0 ** -21
+        we = w * e
+        s_term = 1.01 * (np.einsum("bhqk,bhkd->bhqd", we, np.abs(vf)) + we.sum(-1)[..., None] * np.abs(O[:, :, r0:r1]))
+        if qf.shape[-1] == 64:
+            dev = np.abs(vf[:, :, None, :, :] - O[:, :, r0:r1, None, :])  # [b, h, q, k, d]
+            out[:, :, r0:r1] = np.einsum("bhqk,bhqkd->bhqd", w, dev) * (2.0 ** -7 / (1.0 - 2.0 ** -8))
+        else:
+            out[:, :, r0:r1] = np.einsum("bhqk,bhkd->bhqd", w, np.abs(vf)) * 2.0 ** -8
+        out[:, :, r0:r1] += s_term
+    return out
 
 
 @pytest.mark.parametrize("D", [64, 128])

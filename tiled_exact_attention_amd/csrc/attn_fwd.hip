@@ -287,9 +287,16 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     // P for one pair of S^T values: exponentials, rounding to bf16 (the pair
     // becomes one 32-bit word of the P^T operand) and their sum into rs.
+    // v_dot2 (which sums the rounded pair in one instruction) waits for a
+    // busy matrix core on its SIMD: beside MFMAs a softmax mix with it
+    // issued 2.2x slower than alone, without it 1.3x.  With one softmax wave
+    // per SIMD (8 waves) that wait is exposed, so rs sums the fp32 values
+    // with two adds; with two (16 waves) the other softmax wave issues
+    // during it and the single dot2 is cheaper than two adds.
     // The dot2 operand is the freshly rounded pair itself: hipcc (ROCm 7.2)
     // feeds v_dot2c the wrong register when it is given a bit-cast element
     // of a vector instead.
+    constexpr bool kSumRounded = NW == 16;
     auto exp_pair = [&](int pp, float mu, float rs) -> float {
         const int c4 = pp / 4, j = pp % 4;
         const int kb = c4 >> 1, g0 = 2 * (c4 & 1);
@@ -297,7 +304,8 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         const float p1 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j + 1], c, -mu));
         const bf16x2_t pv2 = {(__bf16)p0, (__bf16)p1};
         pprev[pp / 4][pp % 4] = __builtin_bit_cast(unsigned, pv2);
-        return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
+        if constexpr (kSumRounded) return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
+        else return (rs + p0) + p1;
     };
 
     // ---- matrix phase M(t): O += V(t)^T P(t) (DO_PV), S(t+1) = K(t+1) Q^T
