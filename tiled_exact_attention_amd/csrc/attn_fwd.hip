@@ -70,16 +70,18 @@ constexpr float kMaxTileSum = 256.0f;
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One wave-wide 16-byte-per-lane load from HBM straight into LDS: lane i's
-// 16 bytes from `src` land at LDS byte address `dst` + 16 i (dst must be the
-// same in every lane).  Issued as inline assembly so that the compiler does
-// not treat every later LDS read as a possible reader of this write and wait
-// for the load right away (it cannot tell the buffers apart); the kernel
-// instead waits for all such loads (wait_vmem) before the barrier that hands
-// the buffer to its readers.
-__device__ __forceinline__ void lds_dma16(const void* src, const void* dst)
+// 16 bytes from `base` + `off` (base the same in every lane, off the lane's
+// byte offset) land at LDS byte address `dst` + 16 i (dst the same in every
+// lane).  The wave-uniform base sits in scalar registers and each lane keeps
+// a 32-bit offset, not a 64-bit address.  Issued as inline assembly so that
+// the compiler does not treat every later LDS read as a possible reader of
+// this write and wait for the load right away (it cannot tell the buffers
+// apart); the kernel instead waits for such loads (s_waitcnt vmcnt) before
+// the barrier that hands the buffer to its readers.
+__device__ __forceinline__ void lds_dma16(const void* base, unsigned off, const void* dst)
 {
     const unsigned lds = (unsigned)(uintptr_t)dst;  // low 32 bits of a flat LDS address: the LDS offset
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
 
@@ -211,29 +213,33 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // tiles after tlast hold no key visible to any query of this wave
     const int tlast = !CAUSAL ? ntiles - 1 : (qlast < kbase ? -1 : min(ntiles - 1, (qlast - kbase) / BN));
 
-    // ---- HBM -> LDS: lane `lane` of this wave's j-th load fills 16 bytes
-    // at byte (w * DPW + j) * 1024 + 16 * lane of the tile, i.e. row
-    // drow[j], physical chunk lane % NCH, which holds logical chunk
-    // (lane % NCH) ^ swizzle(row).
+    // ---- HBM -> LDS: lane `lane` of load L fills 16 bytes at byte
+    // L * 1024 + 16 * lane of the tile, i.e. row L * RPI + lane / NCH,
+    // physical chunk lane % NCH, which holds logical chunk
+    // (lane % NCH) ^ swizzle(row).  Rows past the sequence end repeat the
+    // last valid row (their scores are masked, their values meet P = 0).
+    // With fewer loads than waves (NL < NW), K is loaded by waves
+    // 0 .. NL - 1 and V by waves NL .. 2 NL - 1, one load each, so a wave
+    // keeps one row and one chunk offset per lane.
+    const bool wv = NL < NW && w >= NL;
+    const int wrow = (wv ? w - NL : w) * RPI + lane / NCH;
+    const int wchunk = ((lane % NCH) ^ (wv ? v_swz<D>(wrow) : k_swz<D>(wrow))) << 4;
     auto dma = [&](const char* src, uint16_t* tile, bool is_v, int key0) {
         const char* g = src + (int64_t)key0 * 2 * D;
         const int nvalid = Sk - key0;  // >= 1 for every tile loaded
-        int L0 = w * DPW;              // first load of this wave
         if constexpr (NL < NW) {
-            // fewer loads than waves: K by waves 0 .. NL - 1, V by waves
-            // NL .. 2 NL - 1
-            L0 = w - (is_v ? NL : 0);
-            if (L0 < 0 || L0 >= NL) return;
-        }
+            if (is_v != wv || w >= 2 * NL) return;
+            const int srow = wrow < nvalid ? wrow : nvalid - 1;
+            lds_dma16(g, (unsigned)(srow * 2 * D + wchunk), tile + (w - (is_v ? NL : 0)) * 512);
+        } else {
 #pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-            const int row = (L0 + j) * RPI + lane / NCH;
-            const int phys = lane % NCH;
-            const int chunk = phys ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
-            // rows past the sequence end repeat the last valid row (its scores
-            // are masked, its values meet P = 0)
-            const int srow = row < nvalid ? row : nvalid - 1;
-            lds_dma16(g + srow * 2 * D + (chunk << 4), tile + (L0 + j) * 512);
+            for (int j = 0; j < DPW; ++j) {
+                const int L = w * DPW + j;
+                const int row = L * RPI + lane / NCH;
+                const int chunk = (lane % NCH) ^ (is_v ? v_swz<D>(row) : k_swz<D>(row));
+                const int srow = row < nvalid ? row : nvalid - 1;
+                lds_dma16(g, (unsigned)(srow * 2 * D + (chunk << 4)), tile + L * 512);
+            }
         }
     };
 
