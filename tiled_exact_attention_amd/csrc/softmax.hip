@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, 
                                                                 float* __restrict__ m_out, float* __restrict__ l_out)
 {
     constexpr int W = VEC ? (BF16 ? 8 : 4) : 1;  // elements per load
-    constexpr int UN = VEC ? 4 : 16;              // loads per lane per step
+    constexpr int UN = VEC ? (BF16 ? 4 : 8) : 16;  // loads per lane per step
     constexpr int N = UN * W;                     // logits per lane per step
     constexpr int B = BLOCK < N ? BLOCK : N;
     constexpr int NWAVE = WG / 64;
@@ -238,6 +238,8 @@ __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, 
             return;
         }
         if constexpr (VEC) {
+            // fp32 rows are read with non-temporal loads (7% faster at
+            // 1024 x 262144); for bf16 rows they measured 9% slower
             if constexpr (BF16) {
                 const u32x4_t w = *(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(xv) + row * cols) + vi);
 #pragma unroll
@@ -246,7 +248,8 @@ __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, 
                     x[2 * k + 1] = bf16_hi(w[k]);
                 }
             } else {
-                const f32x4v_t w = *(reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(xv) + row * cols) + vi);
+                const f32x4v_t w =
+                    __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(static_cast<const float*>(xv) + row * cols) + vi);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) x[k] = w[k];
             }
@@ -297,12 +300,16 @@ __global__ __launch_bounds__(WG) void row_softmax_stream_kernel(const void* xv, 
     const float mh = mu * kLog2eHi;
     const float ml = fmaf(mu, kLog2eHi, -mh) + mu * kLog2eLo;  // tail of M*log2(e)
     for (int64_t v0 = 0; v0 < nvec; v0 += (int64_t)UN * WG) {
+        // all of the step's loads go out before its first store
+        float xs[N];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) load(v0 + (int64_t)u * WG + t, xs + u * W);
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int64_t vi = v0 + (int64_t)u * WG + t;
             if (vi >= nvec) break;
-            float x[W], y[W];
-            load(vi, x);
+            const float* x = xs + u * W;
+            float y[W];
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 if constexpr (BF16) {
