@@ -208,7 +208,7 @@ def main():
             es = 4 if dt == "f32" else 2
             if name in stages:
                 S[name] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 2 * es,
-                               kind="hbm", kernel="row_softmax", wfrac=0.5,
+                               kind="hbm", kernel="row_softmax", wfrac=0.5, seed=202 if dt == "f32" else 205,
                                workload=f"row_softmax {R}x{C} {dt} N(0,1)x30 block 8")
             if dt == "f32":
                 # the same batch under the other rescale policies (same bits,
@@ -217,7 +217,7 @@ def main():
                     rs, blk = RESCALE_STAGES[n]
                     pol = ("unconditional", "conditional (only when the maximum rose)", "l started at 1")[rs]
                     S[n] = dict(fn=(lambda x=x, y=y, rs=rs, blk=blk: tea.row_softmax_variant(x, rs, out=y, block=blk)),
-                                units=R * C * 8, kind="hbm", kernel="row_softmax", wfrac=0.5,
+                                units=R * C * 8, kind="hbm", kernel="row_softmax", wfrac=0.5, seed=202,
                                 workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block {blk}, rescale {pol}")
             log(f"inputs {name} ready ({time.perf_counter() - t0:.1f}s)")
     if "softmax_long_f32" in stages:
@@ -226,7 +226,7 @@ def main():
         x = inputs.logits(R, C, 30.0, 206, "f32").to(dev)
         y = torch.empty_like(x)
         S["softmax_long_f32"] = dict(fn=(lambda x=x, y=y: tea.row_softmax(x, out=y, block=8)), units=R * C * 12,
-                                     kind="hbm", kernel="row_softmax", wfrac=1 / 3,
+                                     kind="hbm", kernel="row_softmax", wfrac=1 / 3, seed=206,
                                      workload=f"row_softmax {R}x{C} f32 N(0,1)x30 block 8, two reads + one write")
         log(f"inputs softmax_long_f32 ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_nc" in stages:
@@ -235,7 +235,7 @@ def main():
         q, k, v = (t.to(dev) for t in inputs.qkv(B, H, Sq, Sq, D, seed=301))
         o = torch.empty_like(q)
         S["attn_nc"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, causal=False, out=o)),
-                            units=4 * B * H * Sq * Sq * D, kind="mfma", kernel="attn_fwd",
+                            units=4 * B * H * Sq * Sq * D, kind="mfma", kernel="attn_fwd", seed=301,
                             workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 non-causal")
         log(f"inputs attn_nc ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_lowocc" in stages or "attn_lowocc_splitk" in stages:
@@ -246,12 +246,12 @@ def main():
         wl = f"attn_fwd B{B} H{H} Sq{Sq} Sk{Sk} D{D} bf16 non-causal ({(Sq + 255) // 256 * B * H} query blocks)"
         if "attn_lowocc" in stages:
             S["attn_lowocc"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, out=o)),
-                                    units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", workload=wl)
+                                    units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", seed=601, workload=wl)
         if "attn_lowocc_splitk" in stages:
             wsk = torch.empty(tea.attn_fwd_splitk_workspace_bytes(B, H, Sq, D, ns), dtype=torch.uint8, device=dev)
             S["attn_lowocc_splitk"] = dict(
                 fn=(lambda q=q, k=k, v=v, o=o, wsk=wsk, ns=ns: tea.attn_fwd_splitk(q, k, v, ns, workspace=wsk, out=o)),
-                units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", workload=wl + f", {ns} KV splits")
+                units=4 * B * H * Sq * Sk * D, kind="mfma", kernel="attn_fwd", seed=601, workload=wl + f", {ns} KV splits")
         log(f"inputs attn_lowocc ready ({time.perf_counter() - t0:.1f}s)")
     if "attn_causal" in stages:
         w = inputs.WORKLOADS["attn_causal"]
@@ -259,7 +259,7 @@ def main():
         q, k, v = (t.to(dev) for t in inputs.qkv(B, H, Sq, Sq, D, seed=401))
         o = torch.empty_like(q)
         S["attn_causal"] = dict(fn=(lambda q=q, k=k, v=v, o=o: tea.attn_fwd(q, k, v, causal=True, out=o)),
-                                units=4 * B * H * D * Sq * (Sq + 1) // 2, kind="mfma", kernel="attn_fwd",
+                                units=4 * B * H * D * Sq * (Sq + 1) // 2, kind="mfma", kernel="attn_fwd", seed=401,
                                 workload=f"attn_fwd B{B} H{H} S{Sq} D{D} bf16 causal")
         log(f"inputs attn_causal ready ({time.perf_counter() - t0:.1f}s)")
     if "decode" in stages or "decode_fused" in stages:
@@ -274,14 +274,14 @@ def main():
         S["decode"] = dict(fn=(lambda qd=qd, Kd=Kd, Vd=Vd, kvd=kvd, ns=ns, ws=ws, od=od:
                                tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=ns, workspace=ws,
                                                                out=od)),
-                           units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode",
+                           units=tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4, kind="hbm", kernel="decode", seed=501,
                            wfrac=B * H * D * 2 / (tot * H * D * 2 * 2 + B * H * D * 2 * 2 + B * 4),
                            workload=f"decode B{B} H{H} Lmax{Lmax} D{D} bf16 splits{ns} sum(kv_len)={tot}")
         if "decode_fused" in stages:
             of = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
             S["decode_fused"] = dict(fn=(lambda qd=qd, Kd=Kd, Vd=Vd, kvd=kvd, ns=ns, of=of:
                                          tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=ns, out=of)),
-                                     units=S["decode"]["units"], kind="hbm", kernel="decode",
+                                     units=S["decode"]["units"], kind="hbm", kernel="decode", seed=501,
                                      wfrac=S["decode"]["wfrac"],
                                      workload=S["decode"]["workload"] + ", one launch")
         if "decode" not in stages:
@@ -370,7 +370,7 @@ def main():
             ach = s["units"] / (avg * 1e-3) / 1e12
             peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
         paths[n] = {
-            "workload": s["workload"], "in_step": n in names, "avg_ms": round(avg, 5),
+            "workload": s["workload"], "seed": s["seed"], "in_step": n in names, "avg_ms": round(avg, 5),
             "min_ms": round(float(np.min(t)), 5),
             "median_ms": round(float(np.median(t)), 5),
             "roofline": {"bound": s["kind"], "achieved": round(ach, 2), "peak": peak, "unit": unit,
@@ -404,6 +404,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        # inputs: numpy default_rng streams keyed by each stage's seed
+        # (tiled_exact_attention_amd.inputs), bf16 rounded by torch
+        "inputs": {"numpy": np.__version__, "torch": torch.__version__},
         "config": {"workload": hp["workload"], "stages": names, "extra_stages": extras},
         "roofline": hp["roofline"],
         "paths": paths,
