@@ -228,7 +228,7 @@ def test_splitk_parity(D, causal, splits):
 
 def test_splitk_rectangular_and_full_size_sample():
     """Non-causal Sq != Sk with a ragged last tile, and the low-occupancy
-    shape of the bench (B1 H8 Sq1024 Sk65536 D128, 16 splits) on sampled
+    shape of the bench (B1 H8 Sq1024 Sk65536 D128, 8 splits) on sampled
     rows."""
     say("attn_fwd_splitk rectangular 129 x 2049")
     q, k, v = inputs.qkv(2, 2, 129, 2049, 128, seed=77)

@@ -29,7 +29,7 @@ WORKLOADS = {
     "attn_causal": dict(B=2, H=32, S=8192, D=128, causal=True),
     "decode_splitkv": dict(B=16, H=32, Lmax=32768, D=128, num_splits=64),
     # too few query blocks to fill the GPU (32 workgroups): split-K attention
-    "attn_lowocc": dict(B=1, H=8, Sq=1024, Sk=65536, D=128, causal=False, num_splits=16),
+    "attn_lowocc": dict(B=1, H=8, Sq=1024, Sk=65536, D=128, causal=False, num_splits=8),
     # rows longer than 16384: the streaming (two reads, one write) row softmax
     "softmax_long": dict(rows=1024, cols=262144, dtype="f32", scale=30.0),
 }
