@@ -48,6 +48,30 @@ def test_decode_edge_lengths(lengths, splits):
             assert torch.all(o[b, h] == 0)
 
 
+@pytest.mark.parametrize("B", [63, 64, 65, 70])
+def test_decode_many_sequences(B):
+    """Sequences are taken longest first when there are at most 64 of them
+    and in grid order beyond; either way every (b, h) must get its own
+    sequence's result.  Lengths include ties and zeros."""
+    say(f"decode many sequences B={B}")
+    H, D, Lmax = 2, 128, 700
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(0, Lmax + 1, size=B)
+    lengths[::7] = 333  # ties
+    lengths[3] = 0
+    q, K, V, kv = inputs.decode_inputs(B, H, Lmax, D, seed=B, kv_len=lengths)
+    scale = 1.0 / math.sqrt(D)
+    qd, Kd, Vd, kvd = q.to(DEV), K.to(DEV), V.to(DEV), kv.to(DEV)
+    o = tea.attn_decode_splitkv(qd, Kd, Vd, kvd, num_splits=8, scale=scale)
+    of = tea.attn_decode_fused(qd, Kd, Vd, kvd, num_splits=8, scale=scale)
+    torch.cuda.synchronize()
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    ref = _decode_ref(q, K, V, kv.numpy(), scale, pairs)
+    check_attention(to_np(o).reshape(-1, D), ref, f"two launches B={B}")
+    check_attention(to_np(of).reshape(-1, D), ref, f"one launch B={B}")
+    assert torch.all(o[3] == 0) and torch.all(of[3] == 0)
+
+
 def test_decode_d64_and_fp32_out():
     say("decode D=64 fp32 out")
     B, H, D, Lmax = 3, 4, 64, 3000
