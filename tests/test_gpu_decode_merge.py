@@ -211,6 +211,33 @@ def test_merge_unnormalised_bf16_and_identity():
     assert torch.all(z == 0) and torch.all(zm == -math.inf) and torch.all(zl == 0)
 
 
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8, 13, 16, 31, 32])
+@pytest.mark.parametrize("D", [7, 64, 128, 200])
+def test_merge_few_partials_match_padded(S, D):
+    """Up to 32 partials per row are merged by a kernel with one wave per
+    row; padded with empty states to 64 partials the same rows go through
+    the butterfly kernel.  Both build the balanced tree over the partial
+    index (the padding's combines are exact no-ops), so the outputs, m and
+    l agree bit for bit, normalised and not, bf16 and fp32."""
+    say(f"merge few partials S={S} D={D}")
+    N = 300
+    m, l, O = inputs.partials(N, S, D, seed=S * 1000 + D, empty_frac=0.1)
+    pad = 64 - S
+    m2 = torch.cat([m, torch.full((N, pad), -math.inf)], 1)
+    l2 = torch.cat([l, torch.zeros((N, pad))], 1)
+    O2 = torch.cat([O, torch.zeros((N, pad, D))], 1)
+    dm, dl, dO = m.to(DEV), l.to(DEV), O.to(DEV)
+    pm2, pl2, pO2 = m2.to(DEV), l2.to(DEV), O2.to(DEV)
+    for kw in (dict(), dict(normalize=False), dict(out_dtype=torch.bfloat16)):
+        a, am, al = tea.merge_partials(dm, dl, dO, stats=True, **kw)
+        b, bm, bl = tea.merge_partials(pm2, pl2, pO2, stats=True, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"S={S} D={D} {kw}"
+        assert torch.equal(am, bm) and torch.equal(al, bl)
+    mref, lref, Oref, oref = _merge_ref(m, l, O)
+    check_attention(to_np(tea.merge_partials(dm, dl, dO)), oref, f"merge S={S} D={D}")
+
+
 def test_merge_tree_shapes_agree():
     """Merging 64 partials at once, or as two merged halves merged again,
     agrees up to rounding (the combine is associative)."""
