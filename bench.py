@@ -86,7 +86,7 @@ STAGE_KERNELS = {  # stage -> kernels (in launch order) that make up one launch:
     "softmax_long_f32": ["row_softmax_stream_kernel<false, true, 8, 512, 0>"],
     "decode_fused": ["decode_fused_kernel<128, 4, true>"],
     "attn_lowocc": [("attn_fwd_kernel<128, 64, 8, true>", 32 * 512)],
-    "attn_lowocc_splitk": [("attn_fwd_kernel<128, 64, 8, true>", 256 * 512), "merge_kernel<false, true, true>"],
+    "attn_lowocc_splitk": [("attn_fwd_kernel<128, 64, 8, true>", 256 * 512), "merge_rows_kernel<false, true, true, 2>"],
 }
 STAGE_SOURCE = {"softmax_f32": "row_softmax", "softmax_bf16": "row_softmax", "attn_nc": "attn_fwd",
                 "attn_causal": "attn_fwd", "decode": "decode", "softmax_long_f32": "row_softmax",
