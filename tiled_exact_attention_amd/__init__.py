@@ -232,14 +232,15 @@ def attn_decode_fused(q, k, v, kv_len, num_splits: int = 64, scale: float | None
     return o
 
 
-def merge_partials(m, l, O, out_dtype=torch.float32, normalize: bool = True, stats: bool = False):
+def merge_partials(m, l, O, out_dtype=torch.float32, normalize: bool = True, stats: bool = False,
+                   out: torch.Tensor | None = None):
     """Merge partial states m, l [N,S], O [N,S,D] (fp32) into O [N,D]."""
     N, S, D = O.shape
-    o = torch.empty((N, D), dtype=out_dtype, device=O.device)
+    o = torch.empty((N, D), dtype=out_dtype, device=O.device) if out is None else out
     mo = torch.empty(N, dtype=torch.float32, device=O.device) if stats else None
     lo = torch.empty(N, dtype=torch.float32, device=O.device) if stats else None
     _dev(m, l, O, o, mo, lo)
     _check("merge_partials", load_library().merge_partials(_ptr(m), _ptr(l), _ptr(O), N, S, D, _ptr(mo), _ptr(lo),
-                                                           _ptr(o), _dcode(out_dtype), int(bool(normalize)),
+                                                           _ptr(o), _dcode(o.dtype), int(bool(normalize)),
                                                            _stream(O)))
     return (o, mo, lo) if stats else o
