@@ -188,3 +188,43 @@ def test_product_path_does_not_import_the_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in src and "from oracle" not in src and "liboracle" not in src, fn
                 assert "oracle.h" not in src, fn
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The C ABI cannot see a tensor's size, so the binding checks shapes
+    and dtypes against the sizes it passes; these CPU tensors fail there,
+    before anything reaches the library or a device."""
+    import torch
+
+    bf = torch.bfloat16
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="out"):
+        tea.row_softmax(x, out=torch.zeros(4, 7))
+    with pytest.raises(ValueError, match="out"):
+        tea.row_softmax_variant(x, 0, out=torch.zeros(4, 8, dtype=bf))
+    q = torch.zeros(1, 2, 16, 64, dtype=bf)
+    with pytest.raises(ValueError, match="k must be"):
+        tea.attn_fwd(q, torch.zeros(1, 2, 16, 128, dtype=bf), torch.zeros(1, 2, 16, 128, dtype=bf))
+    with pytest.raises(ValueError, match="v must be"):
+        tea.attn_fwd(q, torch.zeros(1, 2, 32, 64, dtype=bf), torch.zeros(1, 2, 16, 64, dtype=bf))
+    with pytest.raises(ValueError, match="out"):
+        tea.attn_fwd(q, q, q, out=torch.zeros(1, 2, 15, 64, dtype=bf))
+    with pytest.raises(ValueError, match="k must be"):
+        tea.attn_fwd_splitk(q, torch.zeros(2, 2, 16, 64, dtype=bf), q, 2)
+    qd = torch.zeros(3, 2, 1, 64, dtype=bf)
+    kd = torch.zeros(3, 2, 100, 64, dtype=bf)
+    kv = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match="kv_len"):
+        tea.attn_decode_splitkv(qd, kd, kd, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="v must be"):
+        tea.attn_decode_fused(qd, kd, torch.zeros(3, 2, 99, 64, dtype=bf), kv)
+    with pytest.raises(ValueError, match="out"):
+        tea.attn_decode_fused(qd, kd, kd, kv, out=torch.zeros(3, 2, 32, dtype=bf))
+    m = torch.zeros(5, 4)
+    O = torch.zeros(5, 4, 8)
+    with pytest.raises(ValueError, match="l must be"):
+        tea.merge_partials(m, torch.zeros(5, 3), O)
+    with pytest.raises(ValueError, match="O must be"):
+        tea.merge_partials(m, m, O.double())
+    with pytest.raises(ValueError, match="out"):
+        tea.merge_partials(m, m, O, out=torch.zeros(5, 4))

@@ -96,6 +96,17 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _shape(name: str, t, shape, dtype=None):
+    """The C ABI takes bare pointers and sizes, so a tensor whose shape or
+    dtype disagrees with the sizes passed would be read or written out of
+    bounds: check it here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or (dtype is not None and t.dtype != dtype):
+        want = f"{tuple(shape)}" + (f" {dtype}" if dtype is not None else "")
+        raise ValueError(f"{name} must be {want}, got {tuple(t.shape)} {t.dtype}")
+
+
 def _dcode(dt: torch.dtype) -> int:
     if dt == torch.float32:
         return TEA_F32
@@ -115,6 +126,7 @@ def row_softmax(x: torch.Tensor, out: torch.Tensor | None = None, block: int = 8
     ``stats=True`` also returns the row maxima and normalisers (fp32)."""
     if x.dim() != 2:
         raise ValueError("x must be [rows, cols]")
+    _shape("out", out, x.shape, x.dtype)
     y = torch.empty_like(x) if out is None else out
     _dev(x, y)
     rows, cols = x.shape
@@ -132,6 +144,7 @@ def row_softmax_variant(x: torch.Tensor, rescale: int, out: torch.Tensor | None 
     as row_softmax for every policy)."""
     if x.dim() != 2:
         raise ValueError("x must be [rows, cols]")
+    _shape("out", out, x.shape, x.dtype)
     y = torch.empty_like(x) if out is None else out
     _dev(x, y)
     rows, cols = x.shape
@@ -148,6 +161,9 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out_dtyp
     """O = softmax(q k^T * scale) v for bf16 q [B,H,Sq,D], k, v [B,H,Sk,D]."""
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
+    _shape("k", k, (B, H, Sk, D))
+    _shape("v", v, (B, H, Sk, D))
+    _shape("out", out, (B, H, Sq, D))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device) if out is None else out
@@ -171,6 +187,9 @@ def attn_fwd_splitk(q, k, v, num_splits: int, scale: float | None = None, causal
     partial states merged; same arguments as attn_fwd."""
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
+    _shape("k", k, (B, H, Sk, D))
+    _shape("v", v, (B, H, Sk, D))
+    _shape("out", out, (B, H, Sq, D))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = attn_fwd_splitk_workspace_bytes(B, H, Sq, D, num_splits)
@@ -198,6 +217,11 @@ def attn_decode_splitkv(q, k, v, kv_len, num_splits: int = 64, scale: float | No
     (device).  Returns O [B,H,D]."""
     B, H, _, D = q.shape
     Lmax = k.shape[2]
+    _shape("q", q, (B, H, 1, D))
+    _shape("k", k, (B, H, Lmax, D))
+    _shape("v", v, (B, H, Lmax, D))
+    _shape("kv_len", kv_len, (B,))
+    _shape("out", out, (B, H, D))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = attn_decode_workspace_bytes(B, H, D, num_splits)
@@ -220,6 +244,11 @@ def attn_decode_fused(q, k, v, kv_len, num_splits: int = 64, scale: float | None
     O [B,H,D]."""
     B, H, _, D = q.shape
     Lmax = k.shape[2]
+    _shape("q", q, (B, H, 1, D))
+    _shape("k", k, (B, H, Lmax, D))
+    _shape("v", v, (B, H, Lmax, D))
+    _shape("kv_len", kv_len, (B,))
+    _shape("out", out, (B, H, D))
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = torch.empty((B, H, D), dtype=out_dtype, device=q.device) if out is None else out
@@ -236,6 +265,10 @@ def merge_partials(m, l, O, out_dtype=torch.float32, normalize: bool = True, sta
                    out: torch.Tensor | None = None):
     """Merge partial states m, l [N,S], O [N,S,D] (fp32) into O [N,D]."""
     N, S, D = O.shape
+    _shape("O", O, (N, S, D), torch.float32)
+    _shape("m", m, (N, S), torch.float32)
+    _shape("l", l, (N, S), torch.float32)
+    _shape("out", out, (N, D))
     o = torch.empty((N, D), dtype=out_dtype, device=O.device) if out is None else out
     mo = torch.empty(N, dtype=torch.float32, device=O.device) if stats else None
     lo = torch.empty(N, dtype=torch.float32, device=O.device) if stats else None
