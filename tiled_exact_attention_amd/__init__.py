@@ -231,6 +231,8 @@ def attn_decode_splitkv(q, k, v, kv_len, num_splits: int = 64, scale: float | No
     _dev(q, k, v, kv_len, o, workspace)
     if kv_len.dtype != torch.int32:
         raise TypeError("kv_len must be int32")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
     _check("attn_decode_splitkv", load_library().attn_decode_splitkv(
         _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o), B, H, Lmax, D, int(num_splits), float(scale),
         _dcode(o.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
@@ -255,6 +257,8 @@ def attn_decode_fused(q, k, v, kv_len, num_splits: int = 64, scale: float | None
     _dev(q, k, v, kv_len, o)
     if kv_len.dtype != torch.int32:
         raise TypeError("kv_len must be int32")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
     _check("attn_decode_fused", load_library().attn_decode_fused(
         _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o), B, H, Lmax, D, int(num_splits), float(scale),
         _dcode(o.dtype), _stream(q)))
