@@ -137,7 +137,8 @@ void oracle_naive_normaliser(const double* x, int64_t n, double* sum_exp, double
  *  12  FAILURE: no guard, so an all -inf first block gives -inf - -inf = NaN
  *  Variants 0..3 and 10..11 apply the guard of reading "empty set": while the
  *  running maximum is still -inf the exponent uses 0 in its place.
- * Traces have one entry per block and may be NULL.  Returns the block count.
+ * Traces have one entry per block; they and the scalar outputs may be NULL.
+ * Returns the block count.
  * ------------------------------------------------------------------------ */
 int64_t oracle_online_trace(const double* x, int64_t n, int64_t block, int variant, double* m_trace,
                             double* l_trace, double* c_trace, int64_t* rescales, double* m_final,
@@ -177,9 +178,9 @@ int64_t oracle_online_trace(const double* x, int64_t n, int64_t block, int varia
         if (l_trace) l_trace[k] = l;
         if (c_trace) c_trace[k] = c;
     }
-    *rescales = nres;
-    *m_final = base2 ? m / LOG2E : m;
-    *l_final = l;
+    if (rescales) *rescales = nres;
+    if (m_final) *m_final = base2 ? m / LOG2E : m;
+    if (l_final) *l_final = l;
     return k;
 }
 

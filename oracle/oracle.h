@@ -22,8 +22,8 @@ void oracle_softmax_f64(const double* x, int64_t n, double* y, double* m, double
 void oracle_naive_normaliser(const double* x, int64_t n, double* sum_exp, double* rel_to_max, int* finite);
 
 /* Online normaliser recurrence over contiguous blocks (see oracle.c for the
- * variants).  Traces are [number of blocks] and nullable.  Returns the block
- * count. */
+ * variants).  Traces are [number of blocks]; they and the scalar outputs are
+ * nullable.  Returns the block count. */
 int64_t oracle_online_trace(const double* x, int64_t n, int64_t block, int variant, double* m_trace,
                             double* l_trace, double* c_trace, int64_t* rescales, double* m_final,
                             double* l_final);
