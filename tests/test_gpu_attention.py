@@ -103,6 +103,27 @@ def test_closed_forms():
     check_attention(to_np(o), O, "scale 30")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(D, causal):
+    """Identical keys give every visible key the same score, so every weight
+    is exactly 1 (2^0) and O is the mean of V over the visible keys (row i's
+    first i + 1 keys when causal), up to the fp32 sums of at most S values."""
+    say(f"attn_fwd identical keys D={D} causal={causal}")
+    S = 333
+    q, k, v = inputs.qkv(1, 2, S, S, D, seed=D + int(causal))
+    k = k[:, :, :1].expand(-1, -1, S, -1).contiguous()
+    o, _, _ = _run(q, k, v, causal, out_dtype=torch.float32)
+    vf = _np32(v).astype(np.float64)
+    if causal:
+        ref = np.cumsum(vf, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    else:
+        ref = np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+    bound = 2.0 * S * 2.0 ** -24 * np.abs(vf).max() + 1e-6
+    err = np.abs(to_np(o) - ref)
+    assert np.max(err) <= bound, f"max err {np.max(err):.2e} > {bound:.2e}"
+
+
 def _ramp_inputs(B, H, Sq, Sk, D, slope, seed):
     """Scores that drift along the keys: q has a unit first component and
     key j's first component is slope * j, so the score of key j rises (or,
