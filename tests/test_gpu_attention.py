@@ -45,7 +45,7 @@ def _run(q, k, v, causal, out_dtype=torch.bfloat16, scale=None):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("S", [1, 2, 17, 64, 127, 128, 129, 300])
+@pytest.mark.parametrize("S", [1, 2, 17, 64, 127, 128, 129, 300, 1000])
 def test_small_full_parity(D, causal, S):
     say(f"attn_fwd small S={S} D={D} causal={causal}")
     q, k, v = inputs.qkv(2, 3, S, S, D, seed=S * 7 + D)
