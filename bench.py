@@ -480,12 +480,12 @@ def cpu_baseline(budget_s: float):
         if t >= budget_s / 4 or rows >= 65536:
             break
         rows = min(65536, int(rows * max(2.0, budget_s / 4 / max(t, 1e-3))))
-    # the whole batch fits in the budget: repeat it so the timing is not a
-    # fraction of a second
+    # then time whole passes over that sample until about budget_s of
+    # oracle work has been measured
     reps = 1
-    while rows >= 65536 and t < budget_s / 4:
+    while t < 0.8 * budget_s:
         s = time.perf_counter()
-        oracle.softmax_rows(x)
+        oracle.softmax_rows(x[:rows])
         t += time.perf_counter() - s
         reps += 1
     bytes_ = rows * C * 8 * reps
