@@ -176,8 +176,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows, heads and KV chunks shard with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows, heads and KV chunks would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
