@@ -134,7 +134,10 @@ size_t attn_fwd_splitk_workspace_bytes(int B, int H, int Sq, int D, int num_spli
  * partial results merge in any order or tree, or across devices).
  *   Arguments as for attn_fwd, plus
  *   num_splits 1 .. 64 (else TEA_EINVAL); tile ranges may be empty (their
- *            partial is the empty state);
+ *            partial is the empty state).  The grid has B * H * query
+ *            blocks * num_splits workgroups (query blocks of 256 rows at
+ *            D = 128, 512 at D = 64), one resident per CU; the fastest
+ *            count measured is the one that fills the 256 CUs once;
  *   workspace device memory of at least attn_fwd_splitk_workspace_bytes(),
  *            16-byte aligned, owned by the caller, overlapping no other
  *            argument; concurrent calls need separate workspaces.
