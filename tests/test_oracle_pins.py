@@ -406,6 +406,9 @@ def test_merge_any_partition_order_tree(n, D, seed, ncuts, data):
     assert mm[0] == m_ref
     if l_ref > 0:
         assert _rel(ll[0], l_ref) <= 1e-14
+        assert np.max(np.abs(OO[0] / ll[0] - O_ref / l_ref)) <= 1e-14
+    else:
+        assert ll[0] == 0.0 and np.all(OO[0] == 0.0)
 
 
 def test_merge_identity_is_bitwise():
@@ -461,3 +464,47 @@ def test_decode_wrapper_matches_attention():
             torch.from_numpy(q[b, h]).double()[None], torch.from_numpy(K[b, h, :L]).double()[None],
             torch.from_numpy(V[b, h, :L]).double()[None], scale=0.5).numpy().reshape(D)
         assert np.max(np.abs(O[n] - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 64, 1024])
+def test_merge_direct_output_matches_attention_of_whole_set(S):
+    """The merged state written out directly (oracle_merge_direct) for N rows
+    of S partials each equals attention over the whole set, for the output as
+    well as the normaliser ([OS-C] One pass, exactly: partial results merge
+    into the result of the whole set, in any order or tree).
+
+    Each row's keys are cut into S contiguous chunks at random points
+    (repeated cut points give empty chunks; with S = 1024 and 300 keys most
+    chunks are empty), each chunk's partial (m, l, unnormalised O) is taken
+    with oracle_partial, and the partials of a row are shuffled before the
+    merge.  The whole-set result comes from oracle_attention, which decimal
+    brute force and torch's scaled_dot_product_attention pin above:
+    O / l matches it to 1e-13, m is the largest score and m + ln l the
+    log-sum-exp.  A row whose partials are all empty merges to (-inf, 0, 0)."""
+    rng = np.random.default_rng(50 + S)
+    N, L, D = 6, 300, 12
+    scale = 0.7
+    q = rng.standard_normal((1, N, 1, D)).astype(np.float32)
+    K = (rng.standard_normal((1, N, L, D)) * 1.5).astype(np.float32)
+    V = rng.standard_normal((1, N, L, D)).astype(np.float32)
+    O_ref, lse_ref = oracle.attention(q, K, V, scale, False)
+    m = np.empty((N + 1, S))
+    l = np.empty((N + 1, S))
+    Op = np.empty((N + 1, S, D))
+    smax = np.empty(N)
+    for n in range(N):
+        s = scale * (K[0, n].astype(np.float64) @ q[0, n, 0].astype(np.float64))
+        smax[n] = s.max()
+        cuts = np.sort(rng.integers(0, L + 1, S - 1))
+        bounds = [0, *cuts.tolist(), L]
+        order = rng.permutation(S)
+        for slot, c in enumerate(order):
+            a, b = bounds[c], bounds[c + 1]
+            m[n, slot], l[n, slot], Op[n, slot] = oracle.partial(s[a:b], V[0, n, a:b].astype(np.float64).reshape(b - a, D))
+    m[N], l[N], Op[N] = -math.inf, 0.0, 0.0  # a row with no key at all
+    mm, ll, OO = oracle.merge_direct(m, l, Op)
+    for n in range(N):
+        assert abs(mm[n] - smax[n]) <= 1e-15 * abs(smax[n])
+        assert np.max(np.abs(OO[n] / ll[n] - O_ref[0, n, 0])) <= 1e-13
+        assert abs(mm[n] + math.log(ll[n]) - lse_ref[0, n, 0]) <= 1e-13
+    assert mm[N] == -math.inf and ll[N] == 0.0 and np.all(OO[N] == 0.0)

@@ -28,6 +28,9 @@ MUTANTS = [
     ("recurrence without correction", "l = l * c + s;", "l = l + s;"),
     ("combine weight index", "O[d] = a1 * O1[d] + a2 * O2[d];", "O[d] = a1 * O1[d] + a1 * O2[d];"),
     ("merge exponent sign", "double a = exp(ms - M);", "double a = exp(M - ms);"),
+    ("merge output index transposed", "o[d] += a * O[(n * S + s) * D + d];", "o[d] += a * O[(s * N + n) * D + d];"),
+    ("merge output weight dropped", "o[d] += a * O[(n * S + s) * D + d];", "o[d] += O[(n * S + s) * D + d];"),
+    ("merge normaliser index transposed", "ksum_add(&acc, a * l[n * S + s]);", "ksum_add(&acc, a * l[s * N + n]);"),
 ]
 
 CHECKS = [
@@ -43,6 +46,8 @@ CHECKS = [
     lambda: pins.test_torch_crosscheck_attention(True, 19, 19),
     pins.test_merge_any_partition_order_tree,
     pins.test_split_kv_chunks_reach_full_decode,
+    lambda: pins.test_merge_direct_output_matches_attention_of_whole_set(7),
+    lambda: pins.test_merge_direct_output_matches_attention_of_whole_set(64),
 ]
 
 
