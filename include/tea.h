@@ -69,6 +69,8 @@ enum tea_dtype { TEA_F32 = 0, TEA_BF16 = 1 };
  *           not depend on it beyond rounding.
  *   m_out   nullable [rows] f32: row maximum (-inf for an empty row).
  *   l_out   nullable [rows] f32: sum over the row of exp(x - m_out).
+ *           m_out and l_out may overlap neither x, y nor each other
+ *           (TEA_EINVAL).
  * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
  */
 int row_softmax(const void* x, void* y, int64_t rows, int64_t cols, int dtype, int block, float* m_out,
@@ -113,7 +115,8 @@ int row_softmax_variant(const void* x, void* y, int64_t rows, int64_t cols, int 
  *   causal  0: every key visible; 1: key j visible to query i iff j <= i,
  *           which requires Sq == Sk (else TEA_EUNSUPPORTED).
  *   lse_out nullable [B, H, Sq] f32: m + ln(l) of the scaled scores
- *           (-inf for a query with no visible key).
+ *           (-inf for a query with no visible key); must not overlap q, k,
+ *           v or o.
  * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int Sq, int Sk, int D,
@@ -166,12 +169,14 @@ size_t attn_decode_workspace_bytes(int B, int H, int D, int num_splits);
  *            Positions >= kv_len[b] are never read.
  *   kv_len   [B] int32 device array; values are clamped to [0, Lmax]; a
  *            sequence of length 0 gives O = 0.
- *   o        [B, H, D] of out_dtype (TEA_BF16 or TEA_F32).
+ *   o        [B, H, D] of out_dtype (TEA_BF16 or TEA_F32); must not overlap
+ *            q, k, v, kv_len or the workspace.
  *   B, H >= 0 (zero: nothing to do); Lmax >= 1; D: 64 or 128 (else
  *            TEA_EUNSUPPORTED); num_splits 1 .. 1024; scale finite, > 0.
  *   workspace device memory of at least attn_decode_workspace_bytes(),
- *            16-byte aligned, owned by the caller, not read before written;
- *            concurrent calls need separate workspaces.
+ *            16-byte aligned, owned by the caller, not read before written,
+ *            overlapping no input; concurrent calls need separate
+ *            workspaces.
  * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
  */
 int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B,
@@ -187,8 +192,8 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32
  * Recognition guide: the Apple decode kernels merge partial results from
  * different simdgroups).  Same chunk bounds, tree and combine as
  * attn_decode_splitkv; the two agree up to rounding.
- *   Arguments as for attn_decode_splitkv, without the workspace;
- *   num_splits 1 .. 64 (else TEA_EINVAL).
+ *   Arguments as for attn_decode_splitkv, without the workspace (o must
+ *   not overlap q, k, v or kv_len); num_splits 1 .. 64 (else TEA_EINVAL).
  * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
  */
 int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B, int H,
@@ -204,7 +209,8 @@ int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t
  *            and normalisers (l = sum exp(x - m) of that partial, >= 0).
  *   O        [N, S, D] f32: unnormalised outputs sum exp(x - m) v.
  *   N >= 0 (0: nothing to do); S 1 .. 65536; D 1 .. 4096.
- *   m_out, l_out nullable [N] f32: merged maximum and normaliser.
+ *   m_out, l_out nullable [N] f32: merged maximum and normaliser; they
+ *            overlap no input, O_out or each other.
  *   O_out    [N, D] of out_dtype: O / l when normalize = 1 (0 where l = 0),
  *            or the merged unnormalised O when normalize = 0 (TEA_F32 only).
  * Returns TEA_OK, TEA_EINVAL or TEA_EHIP.

@@ -228,3 +228,55 @@ def test_binding_rejects_mismatched_tensors():
         tea.merge_partials(m, m, O.double())
     with pytest.raises(ValueError, match="out"):
         tea.merge_partials(m, m, O, out=torch.zeros(5, 4))
+
+
+def test_output_overlap_is_rejected(lib):
+    """Every written region (outputs, statistics, workspaces) must overlap no
+    input and no other output; each such call is rejected before any HIP
+    call (the fake addresses are never dereferenced)."""
+    at = lambda a: ctypes.c_void_p(a)  # noqa: E731
+    # row_softmax: x, y [4, 8] f32 (128 B each); m_out, l_out [4] f32
+    x, y = at(0x10000), at(0x20000)
+    for rs in (lib.row_softmax, lambda *a: lib.row_softmax_variant(*a[:6], tea.TEA_RESCALE_ALWAYS, *a[6:])):
+        assert rs(x, y, 4, 8, tea.TEA_F32, 8, at(0x10000 + 64), NULL, NULL) == tea.TEA_EINVAL  # m_out in x
+        assert rs(x, y, 4, 8, tea.TEA_F32, 8, NULL, at(0x20000 + 124), NULL) == tea.TEA_EINVAL  # l_out in y
+        assert rs(x, y, 4, 8, tea.TEA_F32, 8, at(0x30000), at(0x30000 + 8), NULL) == tea.TEA_EINVAL  # m/l overlap
+        assert rs(x, x, 4, 8, tea.TEA_F32, 8, at(0x10000), NULL, NULL) == tea.TEA_EINVAL  # in place, m_out in x
+    # attn_fwd: q, k, v [1, 1, 8, 64] bf16 (1 KiB each); lse [8] f32
+    A = [at(0x10000), at(0x20000), at(0x30000), at(0x40000)]
+    for lse in (at(0x10000 + 16), at(0x20000), at(0x30000 + 1008)):  # lse inside q, k, v
+        assert lib.attn_fwd(*A, 1, 1, 8, 8, 64, 0.125, 0, tea.TEA_BF16, lse, NULL) == tea.TEA_EINVAL
+        assert lib.attn_fwd_splitk(*A, 1, 1, 8, 8, 64, 0.125, 0, 2, tea.TEA_BF16, lse, at(0x1000000),
+                                   lib.attn_fwd_splitk_workspace_bytes(1, 1, 8, 64, 2), NULL) == tea.TEA_EINVAL
+    # decode: q [2, 2, 1, 128] bf16 (1 KiB), k, v [2, 2, 100, 128] bf16 (100 KiB
+    # each), kv_len [2] int32 (8 B), o [2, 2, 128] bf16 (1 KiB)
+    q, k, v, kv, o = at(0x10000), at(0x100000), at(0x200000), at(0x300000), at(0x400000)
+    need = lib.attn_decode_workspace_bytes(2, 2, 128, 64)
+    W = at(0x1000000)
+
+    def dec(q=q, k=k, v=v, kv=kv, o=o, ws=W):
+        return lib.attn_decode_splitkv(q, k, v, kv, o, 2, 2, 100, 128, 64, 0.1, tea.TEA_BF16, ws, need, NULL)
+
+    def fused(q=q, k=k, v=v, kv=kv, o=o):
+        return lib.attn_decode_fused(q, k, v, kv, o, 2, 2, 100, 128, 64, 0.1, tea.TEA_BF16, NULL)
+
+    for f in (dec, fused):
+        assert f(o=at(0x10000 + 512)) == tea.TEA_EINVAL     # o inside q
+        assert f(o=at(0x100000 + 4096)) == tea.TEA_EINVAL   # o inside k
+        assert f(o=at(0x200000 + 100 * 1024 - 16)) == tea.TEA_EINVAL  # o over the tail of v
+        assert f(o=at(0x300000 - 16)) == tea.TEA_EINVAL     # o runs into kv_len
+    assert dec(ws=at(0x100000)) == tea.TEA_EINVAL           # workspace over k
+    assert dec(ws=at(0x200000 + 1024)) == tea.TEA_EINVAL    # workspace inside v
+    assert dec(ws=at(0x300000 - 256)) == tea.TEA_EINVAL     # workspace over kv_len
+    assert dec(ws=at(0x10000 - 256)) == tea.TEA_EINVAL      # workspace over q
+    # merge_partials: m, l [4, 8] f32 (128 B), O [4, 8, 8] f32 (1 KiB), O_out [4, 8] f32
+    m, l, O, oo = at(0x10000), at(0x20000), at(0x30000), at(0x40000)
+
+    def merge(m_out=NULL, l_out=NULL):
+        return lib.merge_partials(m, l, O, 4, 8, 8, m_out, l_out, oo, tea.TEA_F32, 1, NULL)
+
+    assert merge(m_out=at(0x10000 + 64)) == tea.TEA_EINVAL  # m_out inside m
+    assert merge(l_out=at(0x20000)) == tea.TEA_EINVAL       # l_out over l
+    assert merge(m_out=at(0x30000 + 512)) == tea.TEA_EINVAL  # m_out inside O
+    assert merge(l_out=at(0x40000 + 112)) == tea.TEA_EINVAL  # l_out inside O_out
+    assert merge(at(0x50000), at(0x50000 + 4)) == tea.TEA_EINVAL  # m_out and l_out overlap

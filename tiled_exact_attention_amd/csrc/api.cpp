@@ -21,6 +21,15 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? TEA_OK : TEA_EHIP;
 
 inline bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
 
+// a decode output region [p, p + nb) overlaps one of the decode's inputs: q
+// [B, H, D] bf16, k and v [B, H, Lmax, D] bf16, kv_len [B] int32
+inline bool decode_outputs_overlap_inputs(const void* q, const void* k, const void* v, const int32_t* kv_len,
+                                          int B, int H, int Lmax, int D, const void* p, size_t nb)
+{
+    const size_t qb = (size_t)B * H * D * 2, kb = (size_t)B * H * Lmax * D * 2, lb = (size_t)B * 4;
+    return overlap(p, nb, q, qb) || overlap(p, nb, k, kb) || overlap(p, nb, v, kb) || overlap(p, nb, kv_len, lb);
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +69,12 @@ int row_softmax_variant(const void* x, void* y, int64_t rows, int64_t cols, int 
         if (x != y && overlap(x, bytes, y, bytes)) return TEA_EINVAL;
     }
     if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4))) return TEA_EINVAL;
+    // the row statistics are outputs of their own: they may overlap neither
+    // each other nor the logits or the softmax
+    const size_t sb = (size_t)rows * 4, xb = (size_t)rows * (size_t)cols * es;
+    if (m_out && l_out && overlap(m_out, sb, l_out, sb)) return TEA_EINVAL;
+    for (const float* st : {m_out, l_out})
+        if (st && cols > 0 && (overlap(st, sb, x, xb) || overlap(st, sb, y, xb))) return TEA_EINVAL;
     tea::RowSoftmaxArgs a{x, y, rows, cols, dtype == TEA_BF16, block, m_out, l_out, (hipStream_t)stream};
     a.rescale = rescale == TEA_RESCALE_IF_RISE ? tea::kRescaleIfRise
                 : rescale == TEA_RESCALE_L0_ONE ? tea::kRescaleL0One
@@ -90,7 +105,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
     const size_t qb = (size_t)B * H * Sq * D * 2, kb = (size_t)B * H * Sk * D * 2;
     const size_t ob = (size_t)B * H * Sq * D * (out_dtype == TEA_F32 ? 4 : 2);
     if (overlap(o, ob, q, qb) || (Sk > 0 && (overlap(o, ob, k, kb) || overlap(o, ob, v, kb)))) return TEA_EINVAL;
-    if (lse_out && overlap(lse_out, (size_t)B * H * Sq * 4, o, ob)) return TEA_EINVAL;
+    if (lse_out) {
+        const size_t lb = (size_t)B * H * Sq * 4;
+        if (overlap(lse_out, lb, o, ob) || overlap(lse_out, lb, q, qb) ||
+            (Sk > 0 && (overlap(lse_out, lb, k, kb) || overlap(lse_out, lb, v, kb))))
+            return TEA_EINVAL;
+    }
     tea::AttnArgs a{q, k, v, o, B, H, Sq, Sk, D, scale, causal == 1, out_dtype == TEA_BF16, lse_out,
                     (hipStream_t)stream};
     return status_of(tea::launch_attn_fwd(a));
@@ -127,9 +147,12 @@ int attn_fwd_splitk(const void* q, const void* k, const void* v, void* o, int B,
     if (overlap(workspace, need, o, ob) || overlap(workspace, need, q, qb) ||
         (Sk > 0 && (overlap(workspace, need, k, kb) || overlap(workspace, need, v, kb))))
         return TEA_EINVAL;
-    if (lse_out && (overlap(lse_out, (size_t)B * H * Sq * 4, o, ob) ||
-                    overlap(lse_out, (size_t)B * H * Sq * 4, workspace, need)))
-        return TEA_EINVAL;
+    if (lse_out) {
+        const size_t lb = (size_t)B * H * Sq * 4;
+        if (overlap(lse_out, lb, o, ob) || overlap(lse_out, lb, workspace, need) || overlap(lse_out, lb, q, qb) ||
+            (Sk > 0 && (overlap(lse_out, lb, k, kb) || overlap(lse_out, lb, v, kb))))
+            return TEA_EINVAL;
+    }
     tea::AttnArgs a{q, k, v, o, B, H, Sq, Sk, D, scale, causal == 1, out_dtype == TEA_BF16, lse_out,
                     (hipStream_t)stream};
     return status_of(tea::launch_attn_fwd_splitk(a, num_splits, workspace));
@@ -158,7 +181,11 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32
         return TEA_EINVAL;
     const size_t need = tea::decode_workspace_bytes(B, H, D, num_splits);
     if (workspace_bytes < need) return TEA_EINVAL;
+    // the output and the workspace are written: neither may overlap an
+    // input or the other
     const size_t ob = (size_t)B * H * D * (out_dtype == TEA_F32 ? 4 : 2);
+    if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, o, ob)) return TEA_EINVAL;
+    if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, workspace, need)) return TEA_EINVAL;
     if (overlap(workspace, need, o, ob)) return TEA_EINVAL;
     const size_t n = (size_t)B * H * num_splits;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -184,6 +211,9 @@ int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t
     if (!q || !k || !v || !kv_len || !o) return TEA_EINVAL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(o, 4))
         return TEA_EINVAL;
+    if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, o,
+                                      (size_t)B * H * D * (out_dtype == TEA_F32 ? 4 : 2)))
+        return TEA_EINVAL;
     tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, nullptr, nullptr,
                       nullptr, (hipStream_t)stream};
     return status_of(tea::launch_decode_fused(a));
@@ -203,9 +233,15 @@ int merge_partials(const float* m, const float* l, const float* O, int64_t N, in
         return TEA_EINVAL;
     if ((m_out && !aligned(m_out, 4)) || (l_out && !aligned(l_out, 4))) return TEA_EINVAL;
     const size_t ob = (size_t)N * D * (out_dtype == TEA_F32 ? 4 : 2);
-    if (overlap(O_out, ob, O, (size_t)N * S * D * 4) || overlap(O_out, ob, m, (size_t)N * S * 4) ||
-        overlap(O_out, ob, l, (size_t)N * S * 4))
-        return TEA_EINVAL;
+    const size_t pb = (size_t)N * S * 4, Ob = (size_t)N * S * D * 4, sb = (size_t)N * 4;
+    if (overlap(O_out, ob, O, Ob) || overlap(O_out, ob, m, pb) || overlap(O_out, ob, l, pb)) return TEA_EINVAL;
+    // the merged statistics are outputs too: no overlap with an input, the
+    // merged O or each other
+    if (m_out && l_out && overlap(m_out, sb, l_out, sb)) return TEA_EINVAL;
+    for (const float* st : {m_out, l_out})
+        if (st && (overlap(st, sb, O, Ob) || overlap(st, sb, m, pb) || overlap(st, sb, l, pb) ||
+                   overlap(st, sb, O_out, ob)))
+            return TEA_EINVAL;
     tea::MergeArgs a{m, l, O, N, S, D, m_out, l_out, O_out, out_dtype == TEA_BF16, normalize == 1,
                      (hipStream_t)stream};
     return status_of(tea::launch_merge(a));
