@@ -3,7 +3,8 @@
 Workloads: 4096 x 1024 fp32 logits N(0,1) x {1, 1000} in blocks of 8 and the
 64-logit vector ("The Online Softmax" (curionode), Workshop and One pass,
 exactly); 65536 x 8192 in fp32 and bf16 at scales {1, 30, 1000}, compared on
-sampled rows and by properties that hold at any size; ragged and tiny row
+every 64th row and the first and last 256 rows, and on every row by
+properties that hold at any size; ragged and tiny row
 lengths, every block size, empty rows and in-place operation; rows longer
 than 16384 (up to a million logits), which take the two-read streaming path.
 """
@@ -167,8 +168,9 @@ def test_deterministic():
 
 # ---- 65536 x 8192, the bandwidth-bound workload, at full size ----------------
 
-SAMPLE = np.unique(np.concatenate([np.arange(0, 65536, 1024), np.arange(0, 64), np.arange(65536 - 64, 65536),
-                                   np.random.default_rng(5).integers(0, 65536, 64)]))
+# the sampled mode of the full-size check: every 64th row and the first and
+# last 256 rows (1532 of 65536), compared element by element
+SAMPLE = np.unique(np.concatenate([np.arange(0, 65536, 64), np.arange(0, 256), np.arange(65536 - 256, 65536)]))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -181,19 +183,22 @@ def test_large_config_full_size(dtype, scale):
     y, m, l = tea.row_softmax(x, stats=True)
     torch.cuda.synchronize()
     # every row: finite, in [0, 1], sums to 1 within the elementwise bound
-    # (fp32: 1e-5 relative per term; bf16: 2^-8 rounding per term), maxima
-    # exact
+    # (fp32: 1e-5 relative per term, so 1e-5 on the sum; bf16: 2^-8 rounding
+    # per term), maxima exact
     assert bool(torch.isfinite(y).all()) and bool((y >= 0).all()) and bool((y <= 1).all())
+    worst = 0.0
     for r0 in range(0, 65536, 8192):
         s = y[r0:r0 + 8192].double().sum(dim=1)
-        assert float((s - 1).abs().max()) <= (2e-5 if dtype == "f32" else 4e-3)
+        worst = max(worst, float((s - 1).abs().max()))
+    assert worst <= (1e-5 if dtype == "f32" else 4e-3), f"row sums off by {worst:.2e}"
     assert torch.equal(m, x.float().amax(dim=1))
     assert bool(torch.isfinite(l).all()) and bool((l >= 1).all())
     # sampled rows against the oracle, element by element
     idx = torch.from_numpy(SAMPLE)
     xs = x_cpu[idx]
-    _compare(xs, y.cpu()[idx], m.cpu()[idx], l.cpu()[idx], 1e-5 if dtype == "f32" else 4e-3,
-             f"65536x8192 {dtype} x{scale}")
+    e = _compare(xs, y.cpu()[idx], m.cpu()[idx], l.cpu()[idx], 1e-5 if dtype == "f32" else 4e-3,
+                 f"65536x8192 {dtype} x{scale}")
+    print(f"65536x8192 {dtype} x{scale}: max rel err {e:.3e} over {len(SAMPLE)} rows; row sums within {worst:.2e}")
     del x, y
 
 
