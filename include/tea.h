@@ -15,7 +15,8 @@
  * Conventions for every entry point:
  *   - Pointers named as tensors are DEVICE pointers owned by the caller;
  *     tensors are row-major and contiguous.  The library never allocates,
- *     keeps no pointer after returning and has no mutable global state.
+ *     keeps no pointer after returning and has no mutable global state
+ *     other than the device scratch of attn_decode_splitkv_noalloc.
  *   - `stream` is a hipStream_t (NULL: the default stream).  Every call is
  *     asynchronous on it; results are visible after the stream synchronises.
  *   - Arguments are validated before any HIP call; a failed validation
@@ -43,7 +44,8 @@ enum tea_status {
     TEA_OK = 0,
     TEA_EINVAL = 1,       /* bad argument: null pointer, negative size, bad dtype, misalignment, ... */
     TEA_EUNSUPPORTED = 2, /* valid but not implemented: head_dim, row length, block size */
-    TEA_EHIP = 3          /* the HIP runtime reported an error at launch */
+    TEA_EHIP = 3,         /* the HIP runtime reported an error at launch */
+    TEA_ENOSPACE = 4      /* attn_decode_splitkv_noalloc: the partials would not fit its scratch */
 };
 
 enum tea_dtype { TEA_F32 = 0, TEA_BF16 = 1 };
@@ -182,6 +184,30 @@ size_t attn_decode_workspace_bytes(int B, int H, int D, int num_splits);
 int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B,
                         int H, int Lmax, int D, int num_splits, float scale, int out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_splitkv_noalloc -- attn_decode_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the caller passes inputs and output only,
+ * and the partial states go to a scratch array that the library holds in
+ * device memory, TEA_DECODE_NOALLOC_MAX_BYTES bytes on every GPU it runs on,
+ * kept until the process ends.  Same kernels, chunks and merge tree as
+ * attn_decode_splitkv, so the same bits.
+ *   Arguments as for attn_decode_splitkv, without the workspace.
+ *   The partials need attn_decode_workspace_bytes(B, H, D, num_splits)
+ *   bytes; above TEA_DECODE_NOALLOC_MAX_BYTES the call returns TEA_ENOSPACE
+ *   (B16 H32 D128 with 64 splits needs 17 MB).
+ *   Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ *   The scratch's device address is looked up on the first call on each
+ *   device (with that device current) and cached.  Every call on a GPU shares
+ *   that GPU's scratch, which keeps the last call's partials; each call
+ *   writes every partial before reading it, so nothing needs clearing, but
+ *   calls that overlap on one GPU (concurrent streams or threads) race.
+ * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED, TEA_ENOSPACE or TEA_EHIP.
+ */
+#define TEA_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B,
+                                int H, int Lmax, int D, int num_splits, float scale, int out_dtype, void* stream);
 
 /*
  * attn_decode_fused -- the same decode in one launch and with no workspace:

@@ -280,3 +280,32 @@ def test_output_overlap_is_rejected(lib):
     assert merge(m_out=at(0x30000 + 512)) == tea.TEA_EINVAL  # m_out inside O
     assert merge(l_out=at(0x40000 + 112)) == tea.TEA_EINVAL  # l_out inside O_out
     assert merge(at(0x50000), at(0x50000 + 4)) == tea.TEA_EINVAL  # m_out and l_out overlap
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments like
+    attn_decode_splitkv, and refuses (TEA_ENOSPACE, before any HIP call) a
+    request whose partials exceed the scratch it holds."""
+    f = lib.attn_decode_splitkv_noalloc
+    P = [FAKE, ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000),
+         ctypes.c_void_p(0x50000)]
+
+    def call(B=2, H=2, Lmax=100, D=128, S=64, scale=0.1, od=tea.TEA_BF16, ptrs=P):
+        return f(*ptrs, B, H, Lmax, D, S, scale, od, NULL)
+
+    assert lib.tea_status_string(tea.TEA_ENOSPACE)
+    cap = tea.DECODE_NOALLOC_MAX_BYTES
+    assert lib.attn_decode_workspace_bytes(16, 32, 128, 64) <= cap  # the decode workload fits
+    assert lib.attn_decode_workspace_bytes(64, 32, 128, 64) > cap
+    assert call(B=64, H=32) == tea.TEA_ENOSPACE
+    assert call(B=16, H=32, S=1024) == tea.TEA_ENOSPACE
+    assert call(S=0) == tea.TEA_EINVAL
+    assert call(S=1025) == tea.TEA_EINVAL
+    assert call(D=80) == tea.TEA_EUNSUPPORTED
+    assert call(Lmax=0) == tea.TEA_EINVAL
+    assert call(scale=float("nan")) == tea.TEA_EINVAL
+    assert call(od=3) == tea.TEA_EINVAL
+    assert call(ptrs=[P[0], P[1], P[2], NULL, P[4]]) == tea.TEA_EINVAL
+    assert call(ptrs=[ODD, *P[1:]]) == tea.TEA_EINVAL
+    assert call(ptrs=[*P[:4], ctypes.c_void_p(0x30000 + 64)]) == tea.TEA_EINVAL  # o overlaps v
+    assert call(B=0) == tea.TEA_OK

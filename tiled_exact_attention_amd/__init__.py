@@ -17,12 +17,13 @@ import torch
 
 __all__ = [
     "row_softmax", "attn_fwd", "attn_fwd_splitk", "attn_fwd_splitk_workspace_bytes", "attn_decode_splitkv",
-    "attn_decode_workspace_bytes", "attn_decode_fused", "merge_partials",
+    "attn_decode_workspace_bytes", "attn_decode_splitkv_noalloc", "attn_decode_fused", "merge_partials",
     "TeaError", "library_path", "load_library",
-    "TEA_OK", "TEA_EINVAL", "TEA_EUNSUPPORTED", "TEA_EHIP", "TEA_F32", "TEA_BF16",
+    "TEA_OK", "TEA_EINVAL", "TEA_EUNSUPPORTED", "TEA_EHIP", "TEA_ENOSPACE", "TEA_F32", "TEA_BF16",
 ]
 
-TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED, TEA_EHIP = 0, 1, 2, 3
+TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED, TEA_EHIP, TEA_ENOSPACE = 0, 1, 2, 3, 4
+DECODE_NOALLOC_MAX_BYTES = 32 << 20  # TEA_DECODE_NOALLOC_MAX_BYTES
 TEA_F32, TEA_BF16 = 0, 1
 TEA_RESCALE_ALWAYS, TEA_RESCALE_IF_RISE, TEA_RESCALE_L0_ONE = 0, 1, 2
 
@@ -32,7 +33,7 @@ _lib = None
 _lock = threading.Lock()
 
 EXPORTS = ("row_softmax", "row_softmax_variant", "attn_fwd", "attn_fwd_splitk_workspace_bytes", "attn_fwd_splitk",
-           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_fused",
+           "attn_decode_workspace_bytes", "attn_decode_splitkv", "attn_decode_splitkv_noalloc", "attn_decode_fused",
            "merge_partials",
            "tea_status_string", "tea_abi_version")
 
@@ -68,6 +69,8 @@ def load_library():
             lib.attn_decode_workspace_bytes.restype = SZ
             lib.attn_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, P]
             lib.attn_decode_splitkv.restype = I
+            lib.attn_decode_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
+            lib.attn_decode_splitkv_noalloc.restype = I
             lib.attn_decode_fused.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
             lib.attn_decode_fused.restype = I
             lib.attn_fwd_splitk_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -237,6 +240,31 @@ def attn_decode_splitkv(q, k, v, kv_len, num_splits: int = 64, scale: float | No
         _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(o), B, H, Lmax, D, int(num_splits), float(scale),
         _dcode(o.dtype), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
     return o
+
+
+def attn_decode_splitkv_noalloc(q, k, v, kv_len, out: torch.Tensor, num_splits: int = 64,
+                                scale: float | None = None):
+    """attn_decode_splitkv with the partials in the library's device scratch
+    instead of a workspace: nothing is allocated on this path, so the output
+    ``out`` [B,H,D] (bf16 or fp32) must be passed.  Returns ``out``."""
+    B, H, _, D = q.shape
+    Lmax = k.shape[2]
+    _shape("q", q, (B, H, 1, D))
+    _shape("k", k, (B, H, Lmax, D))
+    _shape("v", v, (B, H, Lmax, D))
+    _shape("kv_len", kv_len, (B,))
+    _shape("out", out, (B, H, D))
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _dev(q, k, v, kv_len, out)
+    if kv_len.dtype != torch.int32:
+        raise TypeError("kv_len must be int32")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    _check("attn_decode_splitkv_noalloc", load_library().attn_decode_splitkv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len), _ptr(out), B, H, Lmax, D, int(num_splits), float(scale),
+        _dcode(out.dtype), _stream(q)))
+    return out
 
 
 def attn_decode_fused(q, k, v, kv_len, num_splits: int = 64, scale: float | None = None,

@@ -6,6 +6,9 @@
 
 #include "launch.hpp"
 
+static_assert(TEA_DECODE_NOALLOC_MAX_BYTES == tea::kDecodeScratchBytes,
+              "the scratch limit stated in tea.h is the size of the device array");
+
 namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -43,6 +46,7 @@ const char* tea_status_string(int status)
     case TEA_EINVAL: return "invalid argument";
     case TEA_EUNSUPPORTED: return "unsupported configuration";
     case TEA_EHIP: return "HIP runtime error";
+    case TEA_ENOSPACE: return "request exceeds the scratch memory of the allocation-free entry point";
     default: return "unknown status";
     }
 }
@@ -187,15 +191,32 @@ int attn_decode_splitkv(const void* q, const void* k, const void* v, const int32
     if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, o, ob)) return TEA_EINVAL;
     if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, workspace, need)) return TEA_EINVAL;
     if (overlap(workspace, need, o, ob)) return TEA_EINVAL;
-    const size_t n = (size_t)B * H * num_splits;
-    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    char* ws = static_cast<char*>(workspace);
-    float* ws_m = reinterpret_cast<float*>(ws);
-    float* ws_l = reinterpret_cast<float*>(ws + up(n * 4));
-    float* ws_O = reinterpret_cast<float*>(ws + 2 * up(n * 4));
-    tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, ws_m, ws_l,
-                      ws_O, (hipStream_t)stream};
+    tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, nullptr, nullptr,
+                      nullptr, (hipStream_t)stream};
+    tea::decode_bind_workspace(a, workspace);
     return status_of(tea::launch_decode(a));
+}
+
+int attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B,
+                                int H, int Lmax, int D, int num_splits, float scale, int out_dtype, void* stream)
+{
+    if (B < 0 || H < 0 || Lmax < 1 || D <= 0) return TEA_EINVAL;
+    if (num_splits < 1 || num_splits > 1024) return TEA_EINVAL;
+    if (out_dtype != TEA_F32 && out_dtype != TEA_BF16) return TEA_EINVAL;
+    if (!good_scale(scale)) return TEA_EINVAL;
+    if (D != 64 && D != 128) return TEA_EUNSUPPORTED;
+    if ((int64_t)B * H == 0) return TEA_OK;
+    if ((int64_t)B * H * num_splits > (int64_t)0x7fffffff) return TEA_EUNSUPPORTED;
+    if (tea::decode_workspace_bytes(B, H, D, num_splits) > tea::kDecodeScratchBytes) return TEA_ENOSPACE;
+    if (!q || !k || !v || !kv_len || !o) return TEA_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(kv_len, 4) || !aligned(o, 4))
+        return TEA_EINVAL;
+    if (decode_outputs_overlap_inputs(q, k, v, kv_len, B, H, Lmax, D, o,
+                                      (size_t)B * H * D * (out_dtype == TEA_F32 ? 4 : 2)))
+        return TEA_EINVAL;
+    tea::DecodeArgs a{q, k, v, kv_len, o, B, H, Lmax, D, num_splits, scale, out_dtype == TEA_BF16, nullptr, nullptr,
+                      nullptr, (hipStream_t)stream};
+    return status_of(tea::launch_decode_noalloc(a));
 }
 
 int attn_decode_fused(const void* q, const void* k, const void* v, const int32_t* kv_len, void* o, int B, int H,

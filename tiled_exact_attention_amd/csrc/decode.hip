@@ -15,12 +15,25 @@
 // base-two units, O unnormalised).  K and V are read from HBM exactly once,
 // with non-temporal loads.
 // Launch 2 (merge.hip): a tree merge of the num_splits partials per (b, h).
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace tea {
 
 hipError_t launch_merge_base2(const MergeArgs& a);
+
+// Partial states of the allocation-free decode (attn_decode_splitkv_noalloc):
+// a file-scope device array, one copy on every GPU the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device memory: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// handed to kernels.  Every call on a GPU shares the GPU's copy and leaves its
+// partials in it; each call writes every partial it reads, so nothing needs
+// clearing, and calls that overlap on one GPU race.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
 
 namespace {
 
@@ -332,6 +345,54 @@ size_t decode_workspace_bytes(int B, int H, int D, int num_splits)
     const size_t n = (size_t)B * H * num_splits;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     return 2 * up(n * sizeof(float)) + up(n * D * sizeof(float));
+}
+
+void decode_bind_workspace(DecodeArgs& a, void* workspace)
+{
+    // m [B H S], l [B H S], O [B H S, D] fp32, each 256-byte aligned
+    const size_t n = (size_t)a.B * a.H * a.num_splits;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    char* ws = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + up(n * 4));
+    a.ws_O = reinterpret_cast<float*>(ws + 2 * up(n * 4));
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of the current device's copy of `scratch`
+hipError_t scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(DecodeArgs a)
+{
+    void* base = nullptr;
+    hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return e;
+    decode_bind_workspace(a, base);
+    return launch_decode(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a)

@@ -59,6 +59,13 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_fused(const DecodeArgs& a);  // ws_* unused
 int decode_fused_max_splits();
 size_t decode_workspace_bytes(int B, int H, int D, int num_splits);
+// points a.ws_m, a.ws_l and a.ws_O into a workspace of decode_workspace_bytes()
+void decode_bind_workspace(DecodeArgs& a, void* workspace);
+// bytes of the device-resident scratch of the allocation-free decode
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+// launch_decode with the partials in that scratch (a.ws_* ignored); the
+// caller has checked decode_workspace_bytes() <= kDecodeScratchBytes
+hipError_t launch_decode_noalloc(DecodeArgs a);
 
 struct AttnArgs {
     const void* q;  // [B, H, Sq, D] bf16
