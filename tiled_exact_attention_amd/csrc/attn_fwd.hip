@@ -13,8 +13,11 @@
 //                    accumulators)
 // so a lane of the 32x32 result owns one query (lane % 32) and half of the
 // keys or dimensions (lane / 32).  The per-query state m, l and the
-// correction alpha are lane-local; the row maximum needs one permlane32 swap,
-// and l is kept as two half sums (one per lane half) added at the end.
+// correction alpha are lane-local; the row maximum needs one permlane32 swap.
+// l sums the same bf16-rounded P that multiplies V: at head dimension 64 as
+// two half sums (one per lane half, v_dot2 in the softmax phase) added at
+// the end, at 128 on the matrix core (v_mfma_f32_16x16x32_bf16 against a
+// 0/1 selector, the full sum in every lane).
 //
 // The MFMA contraction index need not follow key order as long as both
 // operands agree: P^T is used in the order its accumulator registers hold
@@ -63,8 +66,10 @@ __device__ __forceinline__ int v_swz(int row)
     else return ((row >> 1) & 1) << 2;
 }
 
-// largest sum of one lane's P for a tile (32 keys) taken against a row's
-// reference before the reference has to move: no single P then exceeds it
+// how far (base two) a score may exceed its row's reference before the
+// reference has to move: P <= 2^kLag.  The dot2 form checks it through the
+// sum of a lane's P for the tile (32 keys), at most kMaxTileSum = 2^kLag.
+constexpr float kLag = 8.0f;
 constexpr float kMaxTileSum = 256.0f;
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -108,14 +113,16 @@ __device__ __forceinline__ void lds_dma16(const void* base, unsigned off, const 
 // exponential overflows ("Online softmax" (roadmapper), The recurrence and
 // Things that break); any reference r with every score - r small enough
 // serves as well, since O and l are taken relative to the same r and only
-// their ratio is used (and LSE = r + log l).  The softmax phase therefore
-// first takes P against the row's current reference, without the tile
-// maximum; if every lane's sum of P for the tile is at most kMaxTileSum
-// (so no single P exceeds it) that P stands.  Otherwise (and on a row's
-// first tile) the reference moves to the running maximum, O and l are
-// multiplied by 2^(m_old - m_new), and P is taken again: a conditional
-// correction as the pages attribute to Metal FlashAttention ("Online Softmax"
-// (metalworking), Recognition guide), taken one step further.  The
+// their ratio is used (and LSE = r + log l).  The reference moves only when
+// a score of the tile exceeds it by more than 2^kLag (and on a row's first
+// tile): then it moves to the running maximum and O and l are multiplied by
+// 2^(m_old - m_new), a conditional correction as the pages attribute to
+// Metal FlashAttention ("Online Softmax" (metalworking), Recognition guide),
+// taken one step further.  At head dimension 128 the softmax phase checks
+// this with the lane's tile maximum before the exponentials.  At 64 it first
+// takes P against the current reference without the maximum; if every
+// lane's sum of P for the tile is at most kMaxTileSum (so no single P
+// exceeds it) that P stands, otherwise P is taken again after the move.  The
 // reference is always a past running maximum, so some key of the row has
 // P >= 1 and nothing underflows that the exact recurrence keeps; P <= 2^8
 // and l <= Sk 2^8 stay far inside fp32 and bf16 range, and rounding is
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float m = kNegInf, l = 0.0f;
+    float m = kNegInf;
 
     const int kend = CAUSAL ? (Sk < q0 + kBM ? Sk : q0 + kBM) : Sk;
     const int nall = (kend + BN - 1) / BN;
@@ -288,31 +295,76 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     };
 
     f32x16_t sacc[NKB];
-    u32x4_t pprev[NC4];  // P^T operand: P of the current tile as 32-bit words (pairs of bf16)
     constexpr int NPAIR = NKB * 8;  // pairs of S^T values per lane
+
+    // l, the row sum of P, always sums the same bf16-rounded P that
+    // multiplies V, so O = sum p v / sum p is a convex combination of the
+    // values ("Online softmax" (roadmapper), The recurrence: one p feeds
+    // both).  Where the sum is taken depends on the head dimension:
+    //  - D = 64 (16 waves, two softmax waves per SIMD): v_dot2c_f32_bf16 of
+    //    each rounded pair with (1, 1), in the softmax phase.  v_dot2c waits
+    //    for a busy matrix core, but the compiler places the dot2s at the end
+    //    of the phase, when the other group's MFMAs are mostly done, and the
+    //    other softmax wave of the SIMD issues meanwhile; the same sums also
+    //    serve as the check of the lagged reference (below).
+    //  - D = 128 (8 waves, one softmax wave per SIMD, where a waiting dot2
+    //    stalls the SIMD's only softmax wave): on the matrix core, one
+    //    v_mfma_f32_16x16x32_bf16 per 16-key chunk in the matrix phase.
+    constexpr bool kSumOnMatrix = NW == 8;
+    // The P^T operand: separate registers with the dot2 sums (the lagged
+    // reference may still need the scores after P is taken); with the sums
+    // on the matrix core, P is stored in place in the first half of the same
+    // accumulator block: P^T chunk c4 (16 keys) sits in registers
+    // 4 (c4 % 2) .. +3 of sacc[c4 / 2] and is made from registers
+    // 8 (c4 % 2) .. +7, which are read before they are overwritten when the
+    // pairs go in order.  The matrix phase reads every chunk of P before it
+    // starts the next tile's scores in sacc.
+    u32x4_t pprev[kSumOnMatrix ? 1 : NC4];
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    // P for one pair of S^T values: exponentials, rounding to bf16 (the pair
-    // becomes one 32-bit word of the P^T operand) and their sum into rs.
-    // v_dot2 (which sums the rounded pair in one instruction) waits for a
-    // busy matrix core on its SIMD: beside MFMAs a softmax mix with it
-    // issued 2.2x slower than alone, without it 1.3x.  With one softmax wave
-    // per SIMD (8 waves) that wait is exposed, so rs sums the fp32 values
-    // with two adds; with two (16 waves) the other softmax wave issues
-    // during it and the single dot2 is cheaper than two adds.
-    // The dot2 operand is the freshly rounded pair itself: hipcc (ROCm 7.2)
-    // feeds v_dot2c the wrong register when it is given a bit-cast element
-    // of a vector instead.
-    constexpr bool kSumRounded = NW == 16;
+    // P for one pair of S^T values: exponentials, rounding to bf16 and, in
+    // the dot2 form, the pair's sum into rs.  The dot2 operand is the freshly
+    // rounded pair itself: hipcc (ROCm 7.2) feeds v_dot2c the wrong register
+    // when it is given a bit-cast element of a vector instead.
     auto exp_pair = [&](int pp, float mu, float rs) -> float {
         const int c4 = pp / 4, j = pp % 4;
-        const int kb = c4 >> 1, g0 = 2 * (c4 & 1);
-        const float p0 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j], c, -mu));
-        const float p1 = exp2_hw(fmaf(sacc[kb][4 * g0 + 2 * j + 1], c, -mu));
+        const int kb = c4 >> 1, hc = c4 & 1;
+        const float p0 = exp2_hw(fmaf(sacc[kb][8 * hc + 2 * j], c, -mu));
+        const float p1 = exp2_hw(fmaf(sacc[kb][8 * hc + 2 * j + 1], c, -mu));
         const bf16x2_t pv2 = {(__bf16)p0, (__bf16)p1};
-        pprev[pp / 4][pp % 4] = __builtin_bit_cast(unsigned, pv2);
-        if constexpr (kSumRounded) return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
-        else return (rs + p0) + p1;
+        if constexpr (kSumOnMatrix) {
+            sacc[kb][4 * hc + j] = __builtin_bit_cast(float, pv2);
+            return rs;
+        } else {
+            pprev[c4][j] = __builtin_bit_cast(unsigned, pv2);
+            return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
+        }
     };
+    // P^T chunk c4 as the B operand of an MFMA
+    auto pchunk = [&](int c4) -> bf16x8_t {
+        if constexpr (kSumOnMatrix) {
+            const int kb = c4 >> 1, b = 4 * (c4 & 1);
+            const f32x4_t w = {sacc[kb][b], sacc[kb][b + 1], sacc[kb][b + 2], sacc[kb][b + 3]};
+            return __builtin_bit_cast(bf16x8_t, w);
+        } else {
+            return __builtin_bit_cast(bf16x8_t, pprev[c4]);
+        }
+    };
+
+    // The sum on the matrix core: one
+    // v_mfma_f32_16x16x32_bf16 per 16-key chunk takes the P^T operand as its
+    // B operand (lane i: column i % 16, the 8 keys of k-block i / 16) against
+    // a constant A of ones and zeros.  Lane i of the P^T operand holds query
+    // i % 32 and key half i / 32, so k-block g belongs to query column
+    // n + 16 (g % 2); result row r (held by lanes 16 (r / 4) + n) sums the
+    // k-blocks with g % 2 == (r / 4) % 2, i.e. both key halves of exactly the
+    // query that lane owns.  Every lane thus accumulates its query's full
+    // sum of the same bf16-rounded P that multiplies V, and the vector units
+    // spend no instruction on it.
+    const bool lsel_on = ((lane >> 4) & 1) == ((lane >> 2) & 1);
+    const short sel1 = lsel_on ? (short)0x3F80 : (short)0;  // bf16 1.0 or 0
+    const bf16x8_t lsel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
+    f32x4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // matrix-core form: the full row sum in every lane
+    float l = 0.0f;                          // dot2 form: this lane's half of the row sum
 
     // ---- matrix phase M(t): O += V(t)^T P(t) (DO_PV), S(t+1) = K(t+1) Q^T
     // (DO_S).  MFMAs only, with their operands read from LDS through a ring of
@@ -320,6 +372,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     constexpr int NPV = NDB * NC4, NS = NKB * NQC;
     auto mphase = [&](auto pv_c, auto s_c, const char* vt8, const char* kt8) {
         constexpr bool DO_PV = decltype(pv_c)::value, DO_S = decltype(s_c)::value;
+        // the row sum of chunk c4 goes just before its first P V MFMA
         constexpr int N0 = DO_PV ? NPV : 0;
         constexpr int N = N0 + (DO_S ? NS : 0);
         // four waves per SIMD leave room for a ring of two only
@@ -333,8 +386,11 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         for (int j = 0; j < N; ++j) {
             if (j + R - 1 < N) op[(j + R - 1) % R] = rd(j + R - 1);
             if (j < N0) {
-                oacc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], __builtin_bit_cast(bf16x8_t, pprev[j / NDB]),
-                                                                        oacc[j % NDB], 0, 0, 0);
+                if (kSumOnMatrix && j % NDB == 0) {
+                    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pchunk(j / NDB), lacc, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                oacc[j % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[j % R], pchunk(j / NDB), oacc[j % NDB], 0, 0, 0);
             } else {
                 const int i = j - N0, kb = i % NKB, cc = i / NKB;
                 if (cc == 0) {
@@ -361,44 +417,78 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = kNegInf;
         }
-        // fast path: P against the row's current reference, without the
-        // tile maximum.  It stands when every lane's sum of P is at most
-        // 2^kLag (so no single P exceeds it) and the row has a reference.
-        float rs = 0.0f;
-        {
-            const float mu = guard_max(m);
-#pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
-        }
-        const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
-        if (__builtin_amdgcn_ballot_w64(redo)) {
-            // slow path (the first tile of a row, a large rise, or a NaN):
-            // the reference moves to the running maximum, O and l follow it,
-            // and P is taken again against it
+        if constexpr (kSumOnMatrix) {
+            // the lane's tile maximum first (a chain of three-input maxima).
+            // The reference stands while every score of the tile is within
+            // 2^kLag of it, i.e. no P exceeds 2^kLag.
             float mx = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, xor32(mx));
-            const float ms = mx * c;
-            const bool up = ms > m;                   // m = -inf: any finite score moves it
-            const float mn = up ? ms : m;
-            const float mu = guard_max(mn);
-            const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
-            rs = 0.0f;
+            // no reference yet (m = -inf) with a visible key, a rise beyond
+            // the lag, or a NaN: move the reference to the running maximum
+            // (the same for both key halves of a query) and rescale O and l
+            // by 2^(m_old - m_new), exactly 1 where the reference stays
+            if (__builtin_amdgcn_ballot_w64(!(mx * c <= m + kLag))) {
+                mx = fmaxf(mx, xor32(mx));
+                const float ms = mx * c;
+                const bool up = ms > m;                   // m = -inf: any finite score moves it
+                const float mn = up ? ms : m;
+                const float alpha = exp2_hw(m - guard_max(mn));
+                m = mn;
 #pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
-            l *= alpha;
-            m = mn;
-            if (__builtin_amdgcn_ballot_w64(up)) {
+                for (int r = 0; r < 4; ++r) lacc[r] *= alpha;
+                if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                }
             }
+            const float mu = guard_max(m);
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu, 0.0f);
+        } else {
+            // fast path: P against the row's current reference, without the
+            // tile maximum.  It stands when every lane's sum of P is at most
+            // 2^kLag (so no single P exceeds it) and the row has a reference.
+            float rs = 0.0f;
+            {
+                const float mu = guard_max(m);
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+            }
+            const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
+            if (__builtin_amdgcn_ballot_w64(redo)) {
+                // slow path (the first tile of a row, a large rise, or a
+                // NaN): the reference moves to the running maximum, O and l
+                // follow it, and P is taken again against it
+                float mx = kNegInf;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+                mx = fmaxf(mx, xor32(mx));
+                const float ms = mx * c;
+                const bool up = ms > m;                   // m = -inf: any finite score moves it
+                const float mn = up ? ms : m;
+                const float mu = guard_max(mn);
+                const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
+                rs = 0.0f;
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+                l *= alpha;
+                m = mn;
+                if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                }
+            }
+            l += rs;
         }
-        l += rs;
     };
 
     // ---- prologue: K(0), V(0), K(1); every wave computes its S(0) ----------
@@ -445,7 +535,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     }
     if (grp == 0) __syncthreads();  // the barrier of group 1's extra slot
 
-    const float lt = l + xor32(l);
+    const float lt = kSumOnMatrix ? lacc[0] : l + xor32(l);  // the full row sum
     if (nsplit > 1) {
         // ---- partial state for merge_partials: m (natural units), l and
         // unnormalised O, [row, split] with row = (b, h, query) --------------
