@@ -175,12 +175,18 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
     const int nbh = G / (nqb * nsplit);
     if (CAUSAL && nsplit == 1 && G % 8 == 0 && nbh % 8 == 0) {
-        // each XCD owns nbh / 8 heads and takes their query blocks longest
-        // first across its heads: every head's longest block, then every
-        // head's next longest, ...
+        // each XCD owns nbh / 8 heads and takes them two at a time; within a
+        // pair the query blocks go longest first across both heads (the
+        // pair's longest block, then the next longest, ...).  Longest first
+        // shortens the tail of uneven causal blocks; keeping to two heads
+        // keeps the blocks that run at the same time close in their walk
+        // over K and V, so a K/V tile fetched into the XCD's L2 is still
+        // there for the other blocks of its head.
         const int x = bid % 8, local = bid / 8, bhx = nbh / 8;
-        qb = nqb - 1 - local / bhx;
-        bh = (int64_t)x * bhx + local % bhx;
+        const int gh = bhx % 2 == 0 ? 2 : 1;
+        const int per = gh * nqb, gi = local / per, in = local % per;
+        qb = nqb - 1 - in / gh;
+        bh = (int64_t)x * bhx + gi * gh + in % gh;
     }
     const int q0 = qb * kBM;
     const int qrow = q0 + w * 32 + lq;
