@@ -462,17 +462,50 @@ def box_references(dev, stream):
                    "8192^3; medians of 10; frac_of_box = achieved / the rate these give for the same bytes or flops"}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed(fn, budget_s: float):
+    """Run fn() repeatedly until about budget_s has passed; (calls, seconds)."""
+    n, t = 0, 0.0
+    while n == 0 or t < budget_s:
+        s = time.perf_counter()
+        fn()
+        t += time.perf_counter() - s
+        n += 1
+    return n, t
+
+
 def cpu_baseline(budget_s: float):
-    """The fp64 CPU oracle timed on a bounded sample of the headline
-    workload (the first rows of the same 65536 x 8192 fp32 batch), scaled to
-    the metric's unit (GB/s of logits read and written)."""
+    """The fp64 CPU oracle, as it stands, timed on the host cores on bounded
+    samples of the same seeded workloads, each scaled to its stage's unit:
+      value   the headline row softmax 65536 x 8192 fp32 (GB/s of logits read
+              and written), the first rows of the same batch;
+      paths   the 4096 x 1024 softmax on one thread; attention B4 H16 S2048
+              D64 and causal B2 H32 S8192 D128 on every 64th / 256th query
+              row (TFLOP/s of the rows' algorithmic flop); split-KV decode on
+              the 32 heads of two sequences (GB/s of their K and V)."""
+    import numpy as np
+
     import oracle
     from tiled_exact_attention_amd import inputs
 
+    threads = oracle.num_threads()
+    out = {"unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+           "host_cpu_count": os.cpu_count()}
+
+    # headline: the fp32 row softmax, grown to about budget_s / 4 per pass
     C = inputs.WORKLOADS["softmax_large"]["cols"]
     x = inputs.logits(65536, C, 30.0, 202, "f32").numpy()
     rows = 256
-    t = 0.0
     while True:
         s = time.perf_counter()
         oracle.softmax_rows(x[:rows])
@@ -480,19 +513,63 @@ def cpu_baseline(budget_s: float):
         if t >= budget_s / 4 or rows >= 65536:
             break
         rows = min(65536, int(rows * max(2.0, budget_s / 4 / max(t, 1e-3))))
-    # then time whole passes over that sample until about budget_s of
-    # oracle work has been measured
     reps = 1
     while t < 0.8 * budget_s:
         s = time.perf_counter()
         oracle.softmax_rows(x[:rows])
         t += time.perf_counter() - s
         reps += 1
-    bytes_ = rows * C * 8 * reps
-    threads = oracle.num_threads()
-    return {"value": round(bytes_ / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of 65536 rows x {C} fp32 logits (same seeded batch), {reps} pass(es), "
-                      f"fp64 two-pass oracle with OpenMP, {t:.2f}s"}
+    del x
+    out["value"] = round(rows * C * 8 * reps / t / 1e9, 4)
+    out["sample"] = (f"first {rows} of 65536 rows x {C} fp32 logits (same seeded batch), {reps} pass(es), "
+                     f"fp64 two-pass oracle with OpenMP, {t:.2f}s")
+    paths = {}
+
+    # the small softmax configuration on one thread
+    w = inputs.WORKLOADS["softmax_small"]
+    xs = inputs.logits(w["rows"], w["cols"], 1.0, 101, "f32").numpy()
+    prev = oracle.set_num_threads(1)
+    try:
+        n, t = _timed(lambda: oracle.softmax_rows(xs), 2.0)
+    finally:
+        oracle.set_num_threads(prev)
+    paths["softmax_small_1thread"] = {"value": round(xs.size * 8 * n / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                      "sample": f"all {w['rows']} x {w['cols']} fp32 logits x1 (seed 101), {n} pass(es), "
+                                                f"{t:.2f}s"}
+
+    # attention: sampled query rows of the two workloads
+    for name, key, seed, step in (("attn_nc", "attn_noncausal", 301, 64), ("attn_causal", "attn_causal", 401, 256)):
+        w = inputs.WORKLOADS[key]
+        B, H, S, D, causal = w["B"], w["H"], w["S"], w["D"], w["causal"]
+        q, k, v = (a.float().numpy() for a in inputs.qkv(B, H, S, S, D, seed=seed))
+        flat = np.arange(0, B * H * S, step, dtype=np.int64)
+        keys = (flat % S + 1) if causal else np.full(flat.shape, S)
+        flop = int(4 * D * keys.sum())
+        n, t = _timed(lambda: oracle.attention(q, k, v, 1.0 / np.sqrt(D), causal, rows=flat), 2.0)
+        paths[name] = {"value": round(flop * n / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+                       "sample": f"every {step}th of {B * H * S} query rows ({len(flat)} rows, {keys.sum()} visible "
+                                 f"keys) of the seeded workload, {n} pass(es), {t:.2f}s"}
+        del q, k, v
+
+    # split-KV decode: every head of the first two sequences
+    w = inputs.WORKLOADS["decode_splitkv"]
+    B, H, Lmax, D = w["B"], w["H"], w["Lmax"], w["D"]
+    kv_len = inputs.kv_lengths(B, Lmax, 501)
+    qd = inputs.decode_q(B, H, D, 501)
+    sel = [0, 1]
+    data = []
+    for b in sel:
+        L = int(kv_len[b])
+        kk = np.stack([inputs.decode_kv_pair(b, h, L, D, 501)[0] for h in range(H)])[None]
+        vv = np.stack([inputs.decode_kv_pair(b, h, L, D, 501)[1] for h in range(H)])[None]
+        data.append((qd[b][None, :, None, :], kk, vv))
+    nbytes = sum(2 * kk.size * 2 for _, kk, _ in data)  # K and V as bf16
+    n, t = _timed(lambda: [oracle.attention(qq, kk, vv, 1.0 / np.sqrt(D), False) for qq, kk, vv in data], 2.0)
+    paths["decode"] = {"value": round(nbytes * n / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+                       "sample": f"all {H} heads of sequences {sel} (kv_len {[int(kv_len[b]) for b in sel]}) of the "
+                                 f"seeded workload, {n} pass(es), {t:.2f}s"}
+    out["paths"] = paths
+    return out
 
 
 if __name__ == "__main__":

@@ -64,6 +64,8 @@ def _load():
             lib.oracle_merge_direct.argtypes = [P, P, P, I64, I64, I64, P, P, P]
             lib.oracle_abi_version.restype = ctypes.c_int
             lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_num_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -276,3 +278,8 @@ def abi_version() -> int:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops run on."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Run the oracle's OpenMP loops on n threads; returns the previous count."""
+    return int(_load().oracle_set_num_threads(int(n)))

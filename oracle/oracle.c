@@ -374,3 +374,12 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* Run the oracle's OpenMP loops on n threads (n >= 1); used to time it on
+ * one core.  Returns the previous count. */
+int oracle_set_num_threads(int n)
+{
+    int prev = oracle_num_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return prev;
+}

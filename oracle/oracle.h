@@ -51,6 +51,7 @@ void oracle_merge_direct(const double* m, const double* l, const double* O, int6
 
 int oracle_abi_version(void);
 int oracle_num_threads(void);
+int oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

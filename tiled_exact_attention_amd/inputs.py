@@ -124,6 +124,23 @@ def decode_inputs(B: int, H: int, Lmax: int, D: int, seed: int = 0, kv_len=None,
     return _to_torch(q, dtype), K, V, torch.from_numpy(kv_len.copy())
 
 
+def decode_kv_pair(b: int, h: int, L: int, D: int, seed: int = 0):
+    """The valid keys and values of one (b, h) of decode_inputs(..., seed),
+    [L, D] fp32 each after rounding to bf16: the same draws, without
+    building the whole cache."""
+    rk = np.random.default_rng([int(seed), 6, b, h]).standard_normal((L, D), dtype=np.float32)
+    rv = np.random.default_rng([int(seed), 8, b, h]).standard_normal((L, D), dtype=np.float32)
+    widen = lambda a: torch.from_numpy(a).to(torch.bfloat16).float().numpy()  # noqa: E731
+    return widen(rk), widen(rv)
+
+
+def decode_q(B: int, H: int, D: int, seed: int = 0) -> np.ndarray:
+    """The queries of decode_inputs(..., seed), [B, H, D] fp32 after rounding
+    to bf16."""
+    q = _normal_rows(B * H, D, seed, 5).reshape(B, H, D)
+    return torch.from_numpy(q).to(torch.bfloat16).float().numpy()
+
+
 def partials(N: int, S: int, D: int, seed: int = 0, empty_frac: float = 0.0, m_spread: float = 10.0):
     """Random partial states for the merge: m [N,S] (natural units, spread
     over +-m_spread), l [N,S] > 0, O [N,S,D] (unnormalised), fp32; a fraction
