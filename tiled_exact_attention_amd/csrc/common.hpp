@@ -112,6 +112,25 @@ __device__ __forceinline__ float xor16(float v)
     return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
 }
 
+// Value held by lane (lane ^ X), X a power of two below 64, with no LDS
+// traffic: DPP inside each row of 16 lanes (quad permutes for 1 and 2, row
+// rotations for 4 and 8; row_ror:n hands lane i the value of lane
+// (i - n) mod 16), permlane swaps across rows for 16 and 32.
+template <int X>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    static_assert(X == 1 || X == 2 || X == 4 || X == 8 || X == 16 || X == 32, "lane distance");
+    if constexpr (X == 1) return dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+    else if constexpr (X == 2) return dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+    else if constexpr (X == 4) {
+        const float down = dpp_f<0x124>(v);  // row_ror:4:  lane i - 4 (mod 16)
+        const float up = dpp_f<0x12C>(v);    // row_ror:12: lane i + 4 (mod 16)
+        return (__lane_id() & 4) ? down : up;
+    } else if constexpr (X == 8) return dpp_f<0x128>(v);  // row_ror:8
+    else if constexpr (X == 16) return xor16(v);
+    else return xor32(v);
+}
+
 // ---- the guard and the correction -----------------------------------------
 // While a running maximum is still -inf (nothing seen yet, or only masked
 // logits) the exponent is taken relative to 0 instead, so exp2(-inf - -inf)

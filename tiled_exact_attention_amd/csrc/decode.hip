@@ -78,6 +78,33 @@ __device__ __forceinline__ void combine8_1(float& m1, float& l1, float& O1, floa
 // merged by a butterfly over lane groups (both partners combine (lower slot,
 // upper slot) in that order).  On return every lane group holds the chunk's
 // state for its 8 dimensions; maxima are in base-two units.
+// One level of the butterfly that merges the key slots' states: lanes X
+// apart exchange (m, l, O) and both compute combine(lower, upper), so both
+// hold the same bits; then the next level.
+template <int X>
+__device__ __forceinline__ void slot_butterfly(int lane, float& m, float& l, float* O)
+{
+    if constexpr (X < 64) {
+        float mp = lane_xor<X>(m), lp = lane_xor<X>(l), Op[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) Op[d] = lane_xor<X>(O[d]);
+        if (lane & X) {
+            float Om[8], mm = m, lm = l;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                Om[d] = O[d];
+                O[d] = Op[d];
+            }
+            m = mp;
+            l = lp;
+            combine8(m, l, O, mm, lm, Om);
+        } else {
+            combine8(m, l, O, mp, lp, Op);
+        }
+        slot_butterfly<X * 2>(lane, m, l, O);
+    }
+}
+
 template <int D, int U>
 __device__ __forceinline__ void chunk_state(const float* qs, const u32x4_t* kb, const u32x4_t* vb, int64_t k0,
                                             int64_t k1, int lane, float& m, float& l, float* O)
@@ -138,25 +165,9 @@ __device__ __forceinline__ void chunk_state(const float* qs, const u32x4_t* kb, 
         m = mn;
     }
 
-#pragma unroll
-    for (int x = LPK; x < 64; x <<= 1) {
-        float mp = __shfl_xor(m, x), lp = __shfl_xor(l, x), Op[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) Op[d] = __shfl_xor(O[d], x);
-        if (lane & x) {
-            float Om[8], mm = m, lm = l;
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                Om[d] = O[d];
-                O[d] = Op[d];
-            }
-            m = mp;
-            l = lp;
-            combine8(m, l, O, mm, lm, Om);
-        } else {
-            combine8(m, l, O, mp, lp, Op);
-        }
-    }
+    // butterfly over the key slots of the wave (lane distances LPK .. 32),
+    // the exchanges by DPP and permlane swaps
+    slot_butterfly<LPK>(lane, m, l, O);
 }
 
 // q of (b, h) with scale * log2(e) folded in once (scores come out in base

@@ -49,6 +49,33 @@ __device__ __forceinline__ void combine_into(float& m1, float& l1, float* O1, fl
     m1 = m;
 }
 
+// One level of the balanced tree across the wave: lanes X apart exchange
+// their states and both compute combine(lower lane, upper lane), so both
+// hold the same bits; then the next level.
+template <bool BASE2, int X>
+__device__ __forceinline__ void lane_butterfly(int lane, float& m, float& l, float* O)
+{
+    if constexpr (X < 64) {
+        float mp = lane_xor<X>(m), lp = lane_xor<X>(l), Op[kDV];
+#pragma unroll
+        for (int d = 0; d < kDV; ++d) Op[d] = lane_xor<X>(O[d]);
+        if (lane & X) {  // partner is the lower lane: combine(partner, mine)
+            float Om[kDV];
+#pragma unroll
+            for (int d = 0; d < kDV; ++d) Om[d] = O[d];
+            float mm = m, lm = l;
+            m = mp;
+            l = lp;
+#pragma unroll
+            for (int d = 0; d < kDV; ++d) O[d] = Op[d];
+            combine_into<BASE2>(m, l, O, mm, lm, Om);
+        } else {
+            combine_into<BASE2>(m, l, O, mp, lp, Op);
+        }
+        lane_butterfly<BASE2, X * 2>(lane, m, l, O);
+    }
+}
+
 template <bool BASE2, bool OUT_BF16, bool NORMALIZE>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                     const float* __restrict__ pO, int64_t N, int S, int D,
@@ -76,25 +103,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
         combine_into<BASE2>(m, l, O, pm[ps], pl[ps], Ot);
     }
 
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-        float mp = __shfl_xor(m, k), lp = __shfl_xor(l, k), Op[kDV];
-#pragma unroll
-        for (int d = 0; d < kDV; ++d) Op[d] = __shfl_xor(O[d], k);
-        if (lane & k) {  // partner is the lower lane: combine(partner, mine)
-            float Om[kDV];
-#pragma unroll
-            for (int d = 0; d < kDV; ++d) Om[d] = O[d];
-            float mm = m, lm = l;
-            m = mp;
-            l = lp;
-#pragma unroll
-            for (int d = 0; d < kDV; ++d) O[d] = Op[d];
-            combine_into<BASE2>(m, l, O, mm, lm, Om);
-        } else {
-            combine_into<BASE2>(m, l, O, mp, lp, Op);
-        }
-    }
+    // the balanced tree over the 64 lanes' states: lane distances 1 .. 32,
+    // exchanged by DPP and permlane swaps
+    lane_butterfly<BASE2, 1>(lane, m, l, O);
 
     if (lane == 0) {
         if (d0 == 0) {
