@@ -93,13 +93,27 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pm
     float m = kNegInf, l = 0.0f, O[kDV];
 #pragma unroll
     for (int d = 0; d < kDV; ++d) O[d] = 0.0f;
+    // a partial's kDV dimensions as two 16-byte loads when every row start
+    // is 16-byte aligned (D a multiple of 8 and an aligned base, as the
+    // decode's workspace is), else one by one
+    const bool vec = D % kDV == 0 && ((uintptr_t)pO % 16) == 0;
     for (int g = 0; g < G; ++g) {
         const int s = lane * G + g;
         if (s >= S) break;
         const int64_t ps = n * S + s;
         float Ot[kDV];
+        if (vec) {
+            const f32x4v_t a = *reinterpret_cast<const f32x4v_t*>(pO + ps * D + d0);
+            const f32x4v_t b = *reinterpret_cast<const f32x4v_t*>(pO + ps * D + d0 + 4);
 #pragma unroll
-        for (int d = 0; d < kDV; ++d) Ot[d] = (d0 + d < D) ? pO[ps * D + d0 + d] : 0.0f;
+            for (int d = 0; d < 4; ++d) {
+                Ot[d] = a[d];
+                Ot[d + 4] = b[d];
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < kDV; ++d) Ot[d] = (d0 + d < D) ? pO[ps * D + d0 + d] : 0.0f;
+        }
         combine_into<BASE2>(m, l, O, pm[ps], pl[ps], Ot);
     }
 
