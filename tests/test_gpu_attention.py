@@ -218,6 +218,23 @@ def test_drifting_maximum(D, causal, rise):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H", [8, 16, 24, 6])
+def test_causal_grid_orders(D, H):
+    """Causal grids whose (batch, head) count is a multiple of 8 are dealt to
+    the 8 XCDs and walked longest block first within pairs of heads (one
+    head at a time when an XCD's share of heads is odd: H = 8, 24); other
+    grids (H = 6) take the plain reversed order.  Every output row, and the
+    log-sum-exp, must match the oracle whichever order ran."""
+    S = 700  # 2 query blocks at D = 64, 3 at D = 128
+    say(f"attn_fwd causal grid order H={H} D={D}")
+    q, k, v = inputs.qkv(1, H, S, S, D, seed=H * 3 + D)
+    o, lse, scale = _run(q, k, v, True)
+    O, L = oracle.attention(_np32(q), _np32(k), _np32(v), scale, True)
+    check_attention(to_np(o), O, f"causal order H={H} D={D}")
+    assert np.max(np.abs(to_np(lse) - L)) <= LSE_TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("splits", [1, 3, 8, 64])
 def test_splitk_parity(D, causal, splits):
