@@ -160,6 +160,8 @@ def main():
                     help="keep warming up until this much wall time has passed (at least --warmup steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle over every one of the five workloads in full (minutes of CPU work)")
     ap.add_argument("--stages",
                     default=",".join(MAIN_STAGES + EXTRA_STAGES))
     ap.add_argument("--no-box-references", action="store_true",
@@ -419,6 +421,8 @@ def main():
 
     if not args.no_cpu_baseline and "softmax_f32" in S:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if args.cpu_full:
+        out["cpu_full"] = cpu_full()
     print(json.dumps(out), flush=True)
 
 
@@ -570,6 +574,76 @@ def cpu_baseline(budget_s: float):
                                  f"seeded workload, {n} pass(es), {t:.2f}s"}
     out["paths"] = paths
     return out
+
+
+def cpu_full():
+    """The fp64 oracle over each of the five workloads in full, once, on all
+    host threads: every row of the softmax batches (4096 x 1024 at x1 and
+    x1000 with the 64-logit vectors; 65536 x 8192 fp32 and bf16 at x1, x30
+    and x1000), every query row of both attention workloads, every (b, h) of
+    the decode.  Seconds per workload and the rate in each stage's unit."""
+    import numpy as np
+
+    import oracle
+    from tiled_exact_attention_amd import inputs
+
+    res = {"cores": oracle.num_threads(), "cpu_model": cpu_model()}
+
+    def clock(fn):
+        s = time.perf_counter()
+        fn()
+        return time.perf_counter() - s
+
+    w = inputs.WORKLOADS["softmax_small"]
+    t = 0.0
+    for scale, seed in ((1.0, 101), (1000.0, 102)):
+        x = inputs.logits(w["rows"], w["cols"], scale, seed, "f32").numpy()
+        t += clock(lambda: oracle.softmax_rows(x))
+    for scale, seed in ((1.0, 103), (1000.0, 104)):
+        v = inputs.vector64(scale, seed).astype(np.float32)[None]
+        t += clock(lambda: oracle.softmax_rows(v))
+    res["softmax_small"] = {"seconds": round(t, 3), "GB/s": round((2 * w["rows"] * w["cols"] + 2 * 64) * 8 / t / 1e9, 3)}
+    log(f"cpu_full softmax_small {t:.2f}s")
+    w = inputs.WORKLOADS["softmax_large"]
+    t = 0.0
+    for dt, seeds in (("f32", (201, 202, 203)), ("bf16", (204, 205, 206))):
+        for scale, seed in zip((1.0, 30.0, 1000.0), seeds):
+            x = inputs.logits(w["rows"], w["cols"], scale, seed, dt).float().numpy()
+            for r0 in range(0, w["rows"], 8192):  # bounded memory: 8192 rows of fp64 output at a time
+                t += clock(lambda: oracle.softmax_rows(x[r0:r0 + 8192]))
+            del x
+            log(f"cpu_full softmax_large {dt} x{scale} done ({t:.2f}s of oracle so far)")
+    res["softmax_large"] = {"seconds": round(t, 3), "rows": 6 * w["rows"],
+                            "GB/s (fp32-equivalent bytes)": round(6 * w["rows"] * w["cols"] * 8 / t / 1e9, 3)}
+    for name, key, seed in (("attn_nc", "attn_noncausal", 301), ("attn_causal", "attn_causal", 401)):
+        w = inputs.WORKLOADS[key]
+        B, H, S, D, causal = w["B"], w["H"], w["S"], w["D"], w["causal"]
+        q, k, v = (a.float().numpy() for a in inputs.qkv(B, H, S, S, D, seed=seed))
+        t = 0.0
+        step = 8192
+        for r0 in range(0, B * H * S, step):
+            rows = np.arange(r0, min(B * H * S, r0 + step), dtype=np.int64)
+            t += clock(lambda: oracle.attention(q, k, v, 1.0 / np.sqrt(D), causal, rows=rows))
+            if (r0 // step) % 8 == 7:
+                log(f"cpu_full {name}: {r0 + step} of {B * H * S} rows ({t:.1f}s)")
+        flop = 4 * B * H * D * (S * (S + 1) // 2 if causal else S * S)
+        res[name] = {"seconds": round(t, 3), "TFLOP/s": round(flop / t / 1e12, 6)}
+        log(f"cpu_full {name} {t:.2f}s")
+        del q, k, v
+    w = inputs.WORKLOADS["decode_splitkv"]
+    B, H, Lmax, D = w["B"], w["H"], w["Lmax"], w["D"]
+    kv_len = inputs.kv_lengths(B, Lmax, 501)
+    qd = inputs.decode_q(B, H, D, 501)
+    t = 0.0
+    for b in range(B):
+        L = int(kv_len[b])
+        pairs = [inputs.decode_kv_pair(b, h, L, D, 501) for h in range(H)]
+        kk = np.stack([p[0] for p in pairs])[None]
+        vv = np.stack([p[1] for p in pairs])[None]
+        t += clock(lambda: oracle.attention(qd[b][None, :, None, :], kk, vv, 1.0 / np.sqrt(D), False))
+    res["decode"] = {"seconds": round(t, 3), "GB/s": round(int(kv_len.sum()) * H * D * 2 * 2 / t / 1e9, 3)}
+    log(f"cpu_full decode {t:.2f}s")
+    return res
 
 
 if __name__ == "__main__":
