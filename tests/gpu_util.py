@@ -5,7 +5,12 @@ Tolerances (each justified by the arithmetic; the pages ask for a tolerance
 preserved):
   - fp32 softmax: elementwise relative error <= 1e-5 where the reference is a
     normal fp32 number (>= 2^-126); below that, absolute error <= 2^-126
-    (flush to zero accepted).  Outputs finite and in [0, 1].
+    (flush to zero accepted).  A reference within its own relative tolerance
+    of 2^-126 (below 2^-126 * (1 + rel)) may be computed on either side of
+    it, so it falls under the absolute rule (<= 2^-126 * (1 + rel)): the
+    kernel's exponential gives 0 for an exponent below -126 and the rounded
+    exponent of such an element can cross -126.  Outputs finite and in
+    [0, 1].
   - bf16 softmax: elementwise relative <= 4e-3 (bf16 keeps 8 significant
     bits, so rounding to nearest is at most 2^-8 = 3.91e-3 relative, plus the
     fp32 computation), same floor.
@@ -32,14 +37,14 @@ def check_softmax(y: np.ndarray, ref: np.ndarray, rel: float, what: str = ""):
     y = np.asarray(y, np.float64)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     assert np.all(y >= 0.0) and np.all(y <= 1.0), f"{what}: output outside [0, 1]"
-    big = ref >= FLOOR
+    big = ref >= FLOOR * (1.0 + rel)
     err = np.abs(y - ref)
     if np.any(big):
         r = np.max(err[big] / ref[big])
         assert r <= rel, f"{what}: max relative error {r:.3e} > {rel:.1e}"
     if np.any(~big):
         a = np.max(err[~big])
-        assert a <= FLOOR, f"{what}: absolute error {a:.3e} below the normal range"
+        assert a <= FLOOR * (1.0 + rel), f"{what}: absolute error {a:.3e} below the normal range"
     return float(np.max(err[big] / ref[big])) if np.any(big) else 0.0
 
 
