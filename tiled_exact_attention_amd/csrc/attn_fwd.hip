@@ -539,13 +539,13 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         tile(t, std::integral_constant<int, 0>{});
         if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{});
     }
-    if (grp == 0) __syncthreads();  // the barrier of group 1's extra slot
-
-    const float lt = kSumOnMatrix ? lacc[0] : l + xor32(l);  // the full row sum
-    if (nsplit > 1) {
-        // ---- partial state for merge_partials: m (natural units), l and
-        // unnormalised O, [row, split] with row = (b, h, query) --------------
-        if (qrow < Sq) {
+    // the rows' output: (m, l, unnormalised O) for merge_partials with KV
+    // splits, else O / l and the log-sum-exp
+    auto write_out = [&]() __attribute__((always_inline)) {
+        const float lt = kSumOnMatrix ? lacc[0] : l + xor32(l);  // the full row sum
+        if (qrow >= Sq) return;
+        if (nsplit > 1) {
+            // [row, split] with row = (b, h, query); m in natural units
             const int64_t pr = (bh * Sq + qrow) * nsplit + split;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -559,13 +559,9 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
                 pm[pr] = lt > 0.0f ? m * kLn2 : kNegInf;
                 pl[pr] = lt;
             }
+            return;
         }
-        return;
-    }
-
-    // ---- epilogue: O /= l, store, log-sum-exp -----------------------------
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (qrow < Sq) {
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         const int64_t orow = (bh * Sq + qrow) * (int64_t)D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -582,7 +578,13 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
                 }
             }
         if (lse && h == 0) lse[bh * Sq + qrow] = lt > 0.0f ? m * kLn2 + __logf(lt) : kNegInf;
-    }
+    };
+    // ---- epilogue.  Group 0 ran its last matrix phase one slot before group
+    // 1, so it writes its rows first, its stores overlapping group 1's last
+    // matrix phase, and then meets group 1 at the barrier of that extra slot
+    // (no LDS is touched after the loop).
+    write_out();
+    if (grp == 0) __syncthreads();
 }
 
 template <int D, int BN, int NW>
