@@ -14,10 +14,10 @@
 // so a lane of the 32x32 result owns one query (lane % 32) and half of the
 // keys or dimensions (lane / 32).  The per-query state m, l and the
 // correction alpha are lane-local; the row maximum needs one permlane32 swap.
-// l sums the same bf16-rounded P that multiplies V: at head dimension 64 as
-// two half sums (one per lane half, v_dot2 in the softmax phase) added at
-// the end, at 128 on the matrix core (v_mfma_f32_16x16x32_bf16 against a
-// 0/1 selector, the full sum in every lane).
+// l sums the same bf16-rounded P that multiplies V, on the matrix core
+// (v_mfma_f32_16x16x32_bf16 against a 0/1 selector, the full sum in every
+// lane): at head dimension 128 in the matrix phase, at 64 in the softmax
+// phase, where the tile's sum also checks the reference (below).
 //
 // The MFMA contraction index need not follow key order as long as both
 // operands agree: P^T is used in the order its accumulator registers hold
@@ -67,8 +67,9 @@ __device__ __forceinline__ int v_swz(int row)
 }
 
 // how far (base two) a score may exceed its row's reference before the
-// reference has to move: P <= 2^kLag.  The dot2 form checks it through the
-// sum of a lane's P for the tile (32 keys), at most kMaxTileSum = 2^kLag.
+// reference has to move: P <= 2^kLag.  At head dimension 64 it is checked
+// through the row's sum of P for the tile (64 keys), at most
+// kMaxTileSum = 2^kLag.
 constexpr float kLag = 8.0f;
 constexpr float kMaxTileSum = 256.0f;
 
@@ -120,9 +121,9 @@ __device__ __forceinline__ void lds_dma16(const void* base, unsigned off, const 
 // Metal FlashAttention ("Online Softmax" (metalworking), Recognition guide),
 // taken one step further.  At head dimension 128 the softmax phase checks
 // this with the lane's tile maximum before the exponentials.  At 64 it first
-// takes P against the current reference without the maximum; if every
-// lane's sum of P for the tile is at most kMaxTileSum (so no single P
-// exceeds it) that P stands, otherwise P is taken again after the move.  The
+// takes P against the current reference without the maximum; if every row's
+// sum of P for the tile is at most kMaxTileSum (so no single P exceeds it)
+// that P stands, otherwise P is taken again after the move.  The
 // reference is always a past running maximum, so some key of the row has
 // P >= 1 and nothing underflows that the exact recurrence keeps; P <= 2^8
 // and l <= Sk 2^8 stay far inside fp32 and bf16 range, and rounding is
@@ -306,48 +307,39 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // l, the row sum of P, always sums the same bf16-rounded P that
     // multiplies V, so O = sum p v / sum p is a convex combination of the
     // values ("Online softmax" (roadmapper), The recurrence: one p feeds
-    // both).  Where the sum is taken depends on the head dimension:
-    //  - D = 64 (16 waves, two softmax waves per SIMD): v_dot2c_f32_bf16 of
-    //    each rounded pair with (1, 1), in the softmax phase.  v_dot2c waits
-    //    for a busy matrix core, but the compiler places the dot2s at the end
-    //    of the phase, when the other group's MFMAs are mostly done, and the
-    //    other softmax wave of the SIMD issues meanwhile; the same sums also
-    //    serve as the check of the lagged reference (below).
-    //  - D = 128 (8 waves, one softmax wave per SIMD, where a waiting dot2
-    //    stalls the SIMD's only softmax wave): on the matrix core, one
-    //    v_mfma_f32_16x16x32_bf16 per 16-key chunk in the matrix phase.
-    constexpr bool kSumOnMatrix = NW == 8;
-    // The P^T operand: separate registers with the dot2 sums (the lagged
-    // reference may still need the scores after P is taken); with the sums
-    // on the matrix core, P is stored in place in the first half of the same
-    // accumulator block: P^T chunk c4 (16 keys) sits in registers
-    // 4 (c4 % 2) .. +3 of sacc[c4 / 2] and is made from registers
-    // 8 (c4 % 2) .. +7, which are read before they are overwritten when the
-    // pairs go in order.  The matrix phase reads every chunk of P before it
-    // starts the next tile's scores in sacc.
-    u32x4_t pprev[kSumOnMatrix ? 1 : NC4];
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    // P for one pair of S^T values: exponentials, rounding to bf16 and, in
-    // the dot2 form, the pair's sum into rs.  The dot2 operand is the freshly
-    // rounded pair itself: hipcc (ROCm 7.2) feeds v_dot2c the wrong register
-    // when it is given a bit-cast element of a vector instead.
-    auto exp_pair = [&](int pp, float mu, float rs) -> float {
+    // both).  It is taken on the matrix core (below), so the vector units
+    // spend no instruction on it; where depends on the head dimension:
+    //  - D = 128: in the matrix phase, one v_mfma_f32_16x16x32_bf16 per
+    //    16-key chunk accumulated into lacc across tiles, with P stored in
+    //    place in the score accumulators (kPInPlace);
+    //  - D = 64: in the softmax phase, the four chunks' MFMAs into a fresh
+    //    accumulator right after the exponentials.  That tile sum is the
+    //    check of the lagged reference (below) and is then added to l.  P
+    //    goes to separate registers, since the check may need the scores
+    //    again after P is taken.
+    // (A vector sum, v_dot2c_f32_bf16 of each rounded pair with (1, 1), waits
+    // for a busy matrix core and issues 16 more vector instructions per
+    // tile.)
+    constexpr bool kPInPlace = NW == 8;
+    // In place, P^T chunk c4 (16 keys) sits in registers 4 (c4 % 2) .. +3 of
+    // sacc[c4 / 2] and is made from registers 8 (c4 % 2) .. +7, which are
+    // read before they are overwritten when the pairs go in order.  The
+    // matrix phase reads every chunk of P before it starts the next tile's
+    // scores in sacc.
+    u32x4_t pprev[kPInPlace ? 1 : NC4];
+    // P for one pair of S^T values: exponentials and rounding to bf16
+    auto exp_pair = [&](int pp, float mu) {
         const int c4 = pp / 4, j = pp % 4;
         const int kb = c4 >> 1, hc = c4 & 1;
         const float p0 = exp2_hw(fmaf(sacc[kb][8 * hc + 2 * j], c, -mu));
         const float p1 = exp2_hw(fmaf(sacc[kb][8 * hc + 2 * j + 1], c, -mu));
         const bf16x2_t pv2 = {(__bf16)p0, (__bf16)p1};
-        if constexpr (kSumOnMatrix) {
-            sacc[kb][4 * hc + j] = __builtin_bit_cast(float, pv2);
-            return rs;
-        } else {
-            pprev[c4][j] = __builtin_bit_cast(unsigned, pv2);
-            return __builtin_amdgcn_fdot2_f32_bf16(pv2, ones, rs, false);
-        }
+        if constexpr (kPInPlace) sacc[kb][4 * hc + j] = __builtin_bit_cast(float, pv2);
+        else pprev[c4][j] = __builtin_bit_cast(unsigned, pv2);
     };
     // P^T chunk c4 as the B operand of an MFMA
     auto pchunk = [&](int c4) -> bf16x8_t {
-        if constexpr (kSumOnMatrix) {
+        if constexpr (kPInPlace) {
             const int kb = c4 >> 1, b = 4 * (c4 & 1);
             const f32x4_t w = {sacc[kb][b], sacc[kb][b + 1], sacc[kb][b + 2], sacc[kb][b + 3]};
             return __builtin_bit_cast(bf16x8_t, w);
@@ -369,8 +361,15 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     const bool lsel_on = ((lane >> 4) & 1) == ((lane >> 2) & 1);
     const short sel1 = lsel_on ? (short)0x3F80 : (short)0;  // bf16 1.0 or 0
     const bf16x8_t lsel = {sel1, sel1, sel1, sel1, sel1, sel1, sel1, sel1};
-    f32x4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // matrix-core form: the full row sum in every lane
-    float l = 0.0f;                          // dot2 form: this lane's half of the row sum
+    f32x4_t lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // D = 128: the row sum, accumulated in the matrix phase
+    float l = 0.0f;                          // D = 64: the row sum, from the tile sums
+    // D = 64: the row's sum of this tile's P (all four chunks)
+    auto tile_sum = [&]() -> float {
+        f32x4_t ts = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c4 = 0; c4 < NC4; ++c4) ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pchunk(c4), ts, 0, 0, 0);
+        return ts[0];
+    };
 
     // ---- matrix phase M(t): O += V(t)^T P(t) (DO_PV), S(t+1) = K(t+1) Q^T
     // (DO_S).  MFMAs only, with their operands read from LDS through a ring of
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         for (int j = 0; j < N; ++j) {
             if (j + R - 1 < N) op[(j + R - 1) % R] = rd(j + R - 1);
             if (j < N0) {
-                if (kSumOnMatrix && j % NDB == 0) {
+                if (kPInPlace && j % NDB == 0) {
                     lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pchunk(j / NDB), lacc, 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -423,7 +422,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[kb][r] = kNegInf;
         }
-        if constexpr (kSumOnMatrix) {
+        if constexpr (kPInPlace) {
             // the lane's tile maximum first (a chain of three-input maxima).
             // The reference stands while every score of the tile is within
             // 2^kLag of it, i.e. no P exceeds 2^kLag.
@@ -454,17 +453,18 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
             }
             const float mu = guard_max(m);
 #pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu, 0.0f);
+            for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
         } else {
             // fast path: P against the row's current reference, without the
-            // tile maximum.  It stands when every lane's sum of P is at most
-            // 2^kLag (so no single P exceeds it) and the row has a reference.
-            float rs = 0.0f;
+            // tile maximum.  It stands when the row's sum of P for the tile
+            // is at most 2^kLag (so no single P exceeds it) and the row has a
+            // reference.
             {
                 const float mu = guard_max(m);
 #pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+                for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
             }
+            float rs = tile_sum();
             const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
             if (__builtin_amdgcn_ballot_w64(redo)) {
                 // slow path (the first tile of a row, a large rise, or a
@@ -481,9 +481,9 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
                 const float mn = up ? ms : m;
                 const float mu = guard_max(mn);
                 const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
-                rs = 0.0f;
 #pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp) rs = exp_pair(pp, mu, rs);
+                for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
+                rs = tile_sum();
                 l *= alpha;
                 m = mn;
                 if (__builtin_amdgcn_ballot_w64(up)) {
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // the rows' output: (m, l, unnormalised O) for merge_partials with KV
     // splits, else O / l and the log-sum-exp
     auto write_out = [&]() __attribute__((always_inline)) {
-        const float lt = kSumOnMatrix ? lacc[0] : l + xor32(l);  // the full row sum
+        const float lt = kPInPlace ? lacc[0] : l;  // the row sum
         if (qrow >= Sq) return;
         if (nsplit > 1) {
             // [row, split] with row = (b, h, query); m in natural units
