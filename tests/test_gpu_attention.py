@@ -329,3 +329,29 @@ def test_full_size(cfg):
         if (r0 // step) % 2 == 1:
             say(f"attn_fwd full size {cfg}: {r0 + step} of {n} rows compared")
     print(f"{cfg}: max abs err {err:.3e}, LSE {lerr:.3e}, over all {n} rows")
+
+
+@pytest.mark.parametrize("D,H", [(128, 256), (64, 512)])
+def test_beyond_2_31_elements(D, H):
+    """K and V of more than 2^31 elements each (B1, Sk 65549: 2.15e9
+    elements), so the heads near the end sit past byte offset 2^32 and are
+    reached through 64-bit offsets.  16 queries per head (a partial query
+    block) against every key of its head, plain and with 8 KV splits; the
+    first, middle and last heads against the oracle in full."""
+    B, Sq, Sk = 1, 16, 65549
+    assert H * Sk * D > 2 ** 31
+    say(f"attn_fwd past 2^31 elements: B{B} H{H} Sq{Sq} Sk{Sk} D{D}")
+    q = inputs.device_normal((B, H, Sq, D), 611, DEV, dtype="bf16")
+    k = inputs.device_normal((B, H, Sk, D), 612, DEV, dtype="bf16")
+    v = inputs.device_normal((B, H, Sk, D), 613, DEV, dtype="bf16")
+    scale = 1.0 / math.sqrt(D)
+    o, lse = tea.attn_fwd(q, k, v, scale=scale, return_lse=True)
+    o8, lse8 = tea.attn_fwd_splitk(q, k, v, 8, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    for h in (0, 1, H // 2, H - 2, H - 1):
+        sl = slice(h, h + 1)
+        O, L = oracle.attention(_np32(q[:, sl].cpu()), _np32(k[:, sl].cpu()), _np32(v[:, sl].cpu()), scale, False)
+        for name, oo, ll in (("plain", o, lse), ("8 splits", o8, lse8)):
+            check_attention(to_np(oo[:, sl]), O, f"{name} D={D} head {h}")
+            assert np.max(np.abs(to_np(ll[:, sl]) - L)) <= LSE_TOL, f"{name} D={D} head {h}: LSE"
+    del q, k, v

@@ -285,3 +285,36 @@ def test_rescale_variants_match_oracle_and_in_place():
         check_softmax(to_np(y), ref, 1e-5, f"rescale={rescale}")
         assert np.array_equal(to_np(m).astype(np.float64), mref)
         assert to_np(l)[2] == 0.0 and np.all(to_np(y)[2] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beyond_2_31_elements(dtype):
+    """262147 x 8192 logits (2.15e9 elements, N(0,1) x 30): the rows past
+    element 2^31 (row 262144 on) are reached through 64-bit offsets.  The
+    first and last 64 rows (the latter straddle that boundary) and every
+    4096th row against the oracle element by element; every row sums to
+    one."""
+    rows, cols = 262147, 8192
+    assert rows * cols > 2 ** 31
+    say(f"row_softmax past 2^31 elements: {rows}x{cols} {dtype}")
+    x = inputs.device_normal((rows, cols), 621, DEV, scale=30.0, dtype=dtype)
+    y, m, l = tea.row_softmax(x, stats=True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for r0 in range(0, rows, 16384):
+        s = y[r0:r0 + 16384].double().sum(dim=1)
+        worst = max(worst, float((s - 1).abs().max()))
+    assert worst <= (1e-5 if dtype == "f32" else 4e-3), f"row sums off by {worst:.2e}"
+    # sampled rows as contiguous row ranges, each copied to the host as it
+    # lies (torch's index_select on a source past 2^31 elements faulted the
+    # GPU on this ROCm build, so no gather runs on x or y)
+    edge = 2 ** 31 // cols  # the first row past element 2^31
+    assert rows - 64 < edge < rows  # the last 64 rows straddle it
+    ranges = [(0, 64), (rows - 64, rows)] + [(r, r + 1) for r in range(4096, rows - 64, 4096)]
+    for r0, r1 in ranges:
+        ref, mref, lref = oracle.softmax_rows(x[r0:r1].float().cpu().numpy())
+        what = f"{dtype} rows {r0}..{r1}"
+        check_softmax(to_np(y[r0:r1]), ref, 1e-5 if dtype == "f32" else 4e-3, what)
+        assert np.array_equal(to_np(m[r0:r1]).astype(np.float64), mref), what
+        assert np.max(np.abs(to_np(l[r0:r1]) - lref) / lref) <= 1e-5, what
+    del x, y

@@ -8,6 +8,8 @@ Recipe: standard normal fp32 values from ``numpy.random.default_rng`` keyed by
 (seed, chunk index) so that any slice can be drawn on its own and the result
 never depends on the thread count; logits are multiplied by the scale in fp32;
 bf16 tensors are the fp32 values rounded to nearest-even by torch on the CPU.
+Inputs past 2^31 elements are drawn on the device instead (device_normal),
+and the oracle gets slices of them copied back.
 The workshop of "The Online Softmax" (curionode, "Workshop") draws its logits
 the same way: normal values times a chosen scale, in blocks of a chosen size.
 """
@@ -75,6 +77,24 @@ def logits(rows: int, cols: int, scale: float = 1.0, seed: int = 0, dtype: str =
     if scale != 1.0:
         x *= np.float32(scale)
     return _to_torch(x, dtype)
+
+
+def device_normal(shape, seed: int, device, scale: float = 1.0, dtype: str = "f32") -> torch.Tensor:
+    """N(0,1) * scale of the given shape, drawn on `device` by torch's own
+    generator seeded with `seed` (fp32, multiplied by the scale in fp32, bf16
+    rounded to nearest-even from that).  For inputs past 2^31 elements, which
+    would take minutes to draw on the host; the oracle receives slices of the
+    same tensor copied back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "f32":
+        return x
+    raise ValueError(f"unknown dtype {dtype}")
 
 
 def vector64(scale: float = 1.0, seed: int = 0) -> np.ndarray:
