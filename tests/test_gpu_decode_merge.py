@@ -124,6 +124,37 @@ def test_decode_full_size():
           f"kv_len={kv.tolist()}")
 
 
+def test_decode_beyond_2_31_elements():
+    """K and V of 2.15e9 elements each (B4 H64 Lmax 65600 D128, lengths
+    40000, 1, 65599 and 65600): the last sequences' heads sit past element
+    2^31 and are reached through 64-bit offsets.  The padding past each
+    length holds random values (no kernel may read it).  Two-launch (64
+    splits) and one-launch forms; the first, middle and last heads of every
+    sequence against the oracle in full."""
+    B, H, Lmax, D, S = 4, 64, 65600, 128, 64
+    assert B * H * Lmax * D > 2 ** 31
+    say(f"decode past 2^31 elements: B{B} H{H} Lmax{Lmax} D{D} splits{S}")
+    kv = torch.tensor([40000, 1, 65599, 65600], dtype=torch.int32)
+    q = inputs.device_normal((B, H, 1, D), 631, DEV, dtype="bf16")
+    K = inputs.device_normal((B, H, Lmax, D), 632, DEV, dtype="bf16")
+    V = inputs.device_normal((B, H, Lmax, D), 633, DEV, dtype="bf16")
+    scale = 1.0 / math.sqrt(D)
+    kvd = kv.to(DEV)
+    o = tea.attn_decode_splitkv(q, K, V, kvd, num_splits=S, scale=scale)
+    of = tea.attn_decode_fused(q, K, V, kvd, num_splits=S, scale=scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        L = int(kv[b])
+        for h in (0, H // 2, H - 1):
+            ref, _ = oracle.attention(q[b:b + 1, h:h + 1].float().cpu().numpy(),
+                                      K[b:b + 1, h:h + 1, :L].float().cpu().numpy(),
+                                      V[b:b + 1, h:h + 1, :L].float().cpu().numpy(), scale, False)
+            ref = ref.reshape(1, D)
+            check_attention(to_np(o[b, h]).reshape(1, D), ref, f"two launches b={b} h={h} L={L}")
+            check_attention(to_np(of[b, h]).reshape(1, D), ref, f"one launch b={b} h={h} L={L}")
+    del K, V
+
+
 # ---- attn_decode_fused: the single-launch form ------------------------------
 
 @pytest.mark.parametrize("lengths", [[1, 2, 63, 64], [65, 511, 512, 513], [1000, 4096, 32767, 32768], [0, 5, 0, 70]])

@@ -318,3 +318,27 @@ def test_beyond_2_31_elements(dtype):
         assert np.array_equal(to_np(m[r0:r1]).astype(np.float64), mref), what
         assert np.max(np.abs(to_np(l[r0:r1]) - lref) / lref) <= 1e-5, what
     del x, y
+
+
+def test_long_rows_beyond_2_31_elements():
+    """8193 rows of 262144 fp32 logits (2.15e9 elements, N(0,1) x 30) through
+    the streaming (two reads, one write) path: the last row lies past element
+    2^31.  Every row's sum; rows 0, 1, 4096, 8191 and 8192 against the oracle
+    element by element with m and l."""
+    rows, cols = 8193, 262144
+    assert (rows - 1) * cols >= 2 ** 31
+    say(f"row_softmax long rows past 2^31 elements: {rows}x{cols} f32")
+    x = inputs.device_normal((rows, cols), 622, DEV, scale=30.0)
+    y, m, l = tea.row_softmax(x, stats=True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for r0 in range(0, rows, 512):
+        s = y[r0:r0 + 512].double().sum(dim=1)
+        worst = max(worst, float((s - 1).abs().max()))
+    assert worst <= 1e-5, f"row sums off by {worst:.2e}"
+    for r in (0, 1, 4096, rows - 2, rows - 1):
+        ref, mref, lref = oracle.softmax_rows(x[r:r + 1].cpu().numpy())
+        check_softmax(to_np(y[r:r + 1]), ref, 1e-5, f"row {r}")
+        assert np.array_equal(to_np(m[r:r + 1]).astype(np.float64), mref), f"row {r}"
+        assert np.max(np.abs(to_np(l[r:r + 1]) - lref) / lref) <= 1e-5, f"row {r}"
+    del x, y
