@@ -217,7 +217,10 @@ int attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v, con
  * waves' states are combined through LDS ("Online Softmax" (metalworking),
  * Recognition guide: the Apple decode kernels merge partial results from
  * different simdgroups).  Same chunk bounds, tree and combine as
- * attn_decode_splitkv; the two agree up to rounding.
+ * attn_decode_splitkv; the two agree up to rounding.  All of a (batch,
+ * head) runs on one compute unit, so this form fills the GPU only with at
+ * least as many (batch, head) pairs as it has compute units (256 on
+ * MI355X); below that, attn_decode_splitkv is the faster form.
  *   Arguments as for attn_decode_splitkv, without the workspace (o must
  *   not overlap q, k, v or kv_len); num_splits 1 .. 64 (else TEA_EINVAL).
  * Returns TEA_OK, TEA_EINVAL, TEA_EUNSUPPORTED or TEA_EHIP.
