@@ -38,6 +38,7 @@ def _calls():
     wsd = torch.empty(tea.attn_decode_workspace_bytes(3, 4, 128, 16), dtype=torch.uint8, device=DEV)
     od = torch.empty((3, 4, 128), dtype=torch.bfloat16, device=DEV)
     of = torch.empty((3, 4, 128), dtype=torch.bfloat16, device=DEV)
+    on = torch.empty((3, 4, 128), dtype=torch.bfloat16, device=DEV)
     # merge_partials with 8 partials per row (one wave per row) and 64 (butterfly)
     pm8, pl8, pO8 = (t.to(DEV) for t in inputs.partials(500, 8, 128, seed=14, empty_frac=0.1))
     pm64, pl64, pO64 = (t.to(DEV) for t in inputs.partials(100, 64, 96, seed=15, empty_frac=0.1))
@@ -51,6 +52,10 @@ def _calls():
         "attn_decode_splitkv": (lambda: tea.attn_decode_splitkv(qd, K, V, kv, num_splits=16, workspace=wsd, out=od),
                                 [od]),
         "attn_decode_fused": (lambda: tea.attn_decode_fused(qd, K, V, kv, num_splits=16, out=of), [of]),
+        # partials in the library's static scratch: nothing allocated, so it
+        # can be captured once its scratch address is known (first call)
+        "attn_decode_splitkv_noalloc": (lambda: tea.attn_decode_splitkv_noalloc(qd, K, V, kv, on, num_splits=16),
+                                        [on]),
         "merge_partials_8": (lambda: tea.merge_partials(pm8, pl8, pO8, out=om8), [om8]),
         "merge_partials_64": (lambda: tea.merge_partials(pm64, pl64, pO64, out_dtype=torch.bfloat16, out=om64), [om64]),
     }
