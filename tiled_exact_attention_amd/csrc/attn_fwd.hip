@@ -155,6 +155,15 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     static_assert(NL * RPI == BN, "tile rows");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
+    // bf16 output staging.  In the accumulator layout a lane holds 4
+    // dimensions of one query, so a wave's 8-byte stores would touch all 32
+    // of its rows per instruction; through LDS the wave writes its 32 rows
+    // (contiguous in O) 1 KiB per instruction instead.  32 rows per wave,
+    // each padded by 16 bytes so that 16-byte reads stay aligned; one region
+    // per wave of a group (group 0 uses it before the last barrier, group 1
+    // after it).
+    constexpr int ORS = D + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sO[NW / 2][32 * ORS];
 
     // the wave index is uniform: keep it (and all that derives from it) in
     // scalar registers
@@ -543,8 +552,8 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // splits, else O / l and the log-sum-exp
     auto write_out = [&]() __attribute__((always_inline)) {
         const float lt = kPInPlace ? lacc[0] : l;  // the row sum
-        if (qrow >= Sq) return;
         if (nsplit > 1) {
+            if (qrow >= Sq) return;
             // [row, split] with row = (b, h, query); m in natural units
             const int64_t pr = (bh * Sq + qrow) * nsplit + split;
 #pragma unroll
@@ -562,27 +571,55 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
             return;
         }
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const int64_t orow = (bh * Sq + qrow) * (int64_t)D;
+        if constexpr (OUT_BF16) {
+            // the lane id again (mbcnt), so that nothing lane-derived from
+            // before the loop is kept live across it for this
+            const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            const int lq2 = ln & 31, h2 = ln >> 5;
+            uint16_t* so = sO[w % (NW / 2)];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + 8 * g + 4 * h;
-                const float y0 = oacc[db][4 * g] * inv, y1 = oacc[db][4 * g + 1] * inv;
-                const float y2 = oacc[db][4 * g + 2] * inv, y3 = oacc[db][4 * g + 3] * inv;
-                if constexpr (OUT_BF16) {
-                    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(o) + orow + d) =
-                        u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                } else {
-                    *reinterpret_cast<f32x4v_t*>(static_cast<float*>(o) + orow + d) = f32x4v_t{y0, y1, y2, y3};
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + 8 * g + 4 * h2;
+                    const float y0 = oacc[db][4 * g] * inv, y1 = oacc[db][4 * g + 1] * inv;
+                    const float y2 = oacc[db][4 * g + 2] * inv, y3 = oacc[db][4 * g + 3] * inv;
+                    *reinterpret_cast<u32x2_t*>(so + lq2 * ORS + d) = u32x2_t{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
                 }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+            constexpr int CPR = D / 8;  // 16-byte chunks per row
+            // this wave's 32 rows are contiguous in O: a uniform base and a
+            // 32-bit lane offset per chunk
+            char* obase = reinterpret_cast<char*>(static_cast<uint16_t*>(o) + (bh * Sq + q0 + w * 32) * (int64_t)D);
+            const int nrow = Sq - q0 - w * 32;  // rows of this wave inside the sequence
+#pragma unroll
+            for (int j = 0; j < 32 * CPR / 64; ++j) {
+                const int ci = j * 64 + ln, r = ci / CPR, u = ci % CPR;
+                const u32x4_t val = *reinterpret_cast<const u32x4_t*>(so + r * ORS + 8 * u);
+                if (r < nrow) *reinterpret_cast<u32x4_t*>(obase + (unsigned)(r * D + 8 * u) * 2u) = val;
             }
-        if (lse && h == 0) lse[bh * Sq + qrow] = lt > 0.0f ? m * kLn2 + __logf(lt) : kNegInf;
+        } else {
+            if (qrow < Sq) {
+                const int64_t orow = (bh * Sq + qrow) * (int64_t)D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d = db * 32 + 8 * g + 4 * h;
+                        const float y0 = oacc[db][4 * g] * inv, y1 = oacc[db][4 * g + 1] * inv;
+                        const float y2 = oacc[db][4 * g + 2] * inv, y3 = oacc[db][4 * g + 3] * inv;
+                        *reinterpret_cast<f32x4v_t*>(static_cast<float*>(o) + orow + d) = f32x4v_t{y0, y1, y2, y3};
+                    }
+            }
+        }
+        if (lse && h == 0 && qrow < Sq) lse[bh * Sq + qrow] = lt > 0.0f ? m * kLn2 + __logf(lt) : kNegInf;
     };
     // ---- epilogue.  Group 0 ran its last matrix phase one slot before group
     // 1, so it writes its rows first, its stores overlapping group 1's last
-    // matrix phase, and then meets group 1 at the barrier of that extra slot
-    // (no LDS is touched after the loop).
+    // matrix phase, and then meets group 1 at the barrier of that extra slot.
+    // After the loop only the staging area sO is touched in LDS: by group 0
+    // before that barrier (group 1 is then reading only K and V), by group 1
+    // after it, when group 0's reads of sO have returned.
     write_out();
     if (grp == 0) __syncthreads();
 }
