@@ -155,15 +155,15 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     static_assert(NL * RPI == BN, "tile rows");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE];
-    // bf16 output staging.  In the accumulator layout a lane holds 4
-    // dimensions of one query, so a wave's 8-byte stores would touch all 32
-    // of its rows per instruction; through LDS the wave writes its 32 rows
-    // (contiguous in O) 1 KiB per instruction instead.  32 rows per wave,
-    // each padded by 16 bytes so that 16-byte reads stay aligned; one region
-    // per wave of a group (group 0 uses it before the last barrier, group 1
-    // after it).
+    // Staging of each wave's 32 rows of Q (in the prologue) and of O (bf16,
+    // in the epilogue).  In the operand and accumulator layouts a lane holds
+    // a few dimensions of one query, so a wave's direct loads and stores
+    // would touch all 32 of its rows per instruction; through LDS the wave
+    // reads Q and writes O (32 rows, contiguous in HBM) 1 KiB per
+    // instruction instead.  One region per wave, rows padded by 16 bytes so
+    // that 16-byte accesses stay aligned.
     constexpr int ORS = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sO[NW / 2][32 * ORS];
+    __shared__ __attribute__((aligned(16))) uint16_t sO[NW][32 * ORS];
 
     // the wave index is uniform: keep it (and all that derives from it) in
     // scalar registers
@@ -207,17 +207,22 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     const char* vp = reinterpret_cast<const char*>(v + bh * (int64_t)Sk * D);
 
     // Q^T operand: lane (query lq, half h) holds Q[q][16c + 8h .. +8)
-    bf16x8_t qop[NQC];
-    {
-        const bool ok = qrow < Sq;
-        const int qr = ok ? qrow : Sq - 1;
+    // Q: the wave's 32 rows are contiguous, so lane i of load j takes 16-byte
+    // chunk j * 64 + i of them (1 KiB per instruction); the rows go through
+    // the wave's LDS staging region into the operand layout after the
+    // prologue's wait.  Rows past the sequence read its last row and are
+    // zeroed.
+    constexpr int QCPR = D / 8;               // 16-byte chunks per row
+    constexpr int NQL = 32 * QCPR / 64;       // such loads per lane
+    u32x4_t qld[NQL];
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) {
-            u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(qp + (int64_t)qr * D + 16 * cc + 8 * h);
-            if (!ok) t4 = u32x4_t{0u, 0u, 0u, 0u};
-            qop[cc] = __builtin_bit_cast(bf16x8_t, t4);
-        }
+    for (int j = 0; j < NQL; ++j) {
+        const int ci = j * 64 + lane, r = ci / QCPR, u = ci % QCPR;
+        const int row = q0 + w * 32 + r;
+        qld[j] = *reinterpret_cast<const u32x4_t*>(qp + (int64_t)(row < Sq ? row : Sq - 1) * D + 8 * u);
+        if (row >= Sq) qld[j] = u32x4_t{0u, 0u, 0u, 0u};
     }
+    bf16x8_t qop[NQC];
 
     f32x16_t oacc[NDB];
 #pragma unroll
@@ -513,6 +518,18 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         if (ntiles > 1) dma(kp, sK[1], false, kbase + BN);
     }
     wait_vmem();
+    {
+        uint16_t* sq = sO[w];
+#pragma unroll
+        for (int j = 0; j < NQL; ++j) {
+            const int ci = j * 64 + lane, r = ci / QCPR, u = ci % QCPR;
+            *reinterpret_cast<u32x4_t*>(sq + r * ORS + 8 * u) = qld[j];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's Q rows are in LDS
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc)
+            qop[cc] = *reinterpret_cast<const bf16x8_t*>(sq + lq * ORS + 8 * (2 * cc + h));
+    }
     __syncthreads();
     if (ntiles > 0) mphase(std::false_type{}, std::true_type{}, nullptr, reinterpret_cast<const char*>(sK[0]));
     if (grp == 1) __syncthreads();  // group 1 runs one slot behind group 0
@@ -576,7 +593,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
             // before the loop is kept live across it for this
             const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
             const int lq2 = ln & 31, h2 = ln >> 5;
-            uint16_t* so = sO[w % (NW / 2)];
+            uint16_t* so = sO[w];
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -617,9 +634,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     // ---- epilogue.  Group 0 ran its last matrix phase one slot before group
     // 1, so it writes its rows first, its stores overlapping group 1's last
     // matrix phase, and then meets group 1 at the barrier of that extra slot.
-    // After the loop only the staging area sO is touched in LDS: by group 0
-    // before that barrier (group 1 is then reading only K and V), by group 1
-    // after it, when group 0's reads of sO have returned.
+    // After the loop only each wave's own staging region is touched in LDS.
     write_out();
     if (grp == 0) __syncthreads();
 }
