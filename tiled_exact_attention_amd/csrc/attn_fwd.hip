@@ -511,7 +511,9 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         }
     };
 
-    // ---- prologue: K(0), V(0), K(1); every wave computes its S(0) ----------
+    // ---- prologue: K(0), V(0), K(1) into LDS; each wave's rows of Q, loaded
+    // at the start, go through its staging region into the operand layout;
+    // every wave computes its S(0) ------------------------------------------
     if (ntiles > 0) {
         dma(kp, sK[0], false, kbase);
         dma(vp, sV[0], true, kbase);
