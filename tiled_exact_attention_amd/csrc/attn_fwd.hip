@@ -16,8 +16,8 @@
 // correction alpha are lane-local; the row maximum needs one permlane32 swap.
 // l sums the same bf16-rounded P that multiplies V, on the matrix core
 // (v_mfma_f32_16x16x32_bf16 against a 0/1 selector, the full sum in every
-// lane): at head dimension 128 in the matrix phase, at 64 in the softmax
-// phase, where the tile's sum also checks the reference (below).
+// lane), in the matrix phase; at head dimension 64 the tile's sum also
+// checks the reference (below), before that P meets V.
 //
 // The MFMA contraction index need not follow key order as long as both
 // operands agree: P^T is used in the order its accumulator registers hold
@@ -120,10 +120,11 @@ __device__ __forceinline__ void lds_dma16(const void* base, unsigned off, const 
 // 2^(m_old - m_new), a conditional correction as the pages attribute to
 // Metal FlashAttention ("Online Softmax" (metalworking), Recognition guide),
 // taken one step further.  At head dimension 128 the softmax phase checks
-// this with the lane's tile maximum before the exponentials.  At 64 it first
-// takes P against the current reference without the maximum; if every row's
-// sum of P for the tile is at most kMaxTileSum (so no single P exceeds it)
-// that P stands, otherwise P is taken again after the move.  The
+// this with the lane's tile maximum before the exponentials.  At 64 it
+// takes P against the current reference without the maximum, and the
+// matrix phase checks that P before its first product with V: if every
+// row's sum of P for the tile is at most kMaxTileSum (so no single P
+// exceeds it) that P stands, otherwise P is taken again after the move.  The
 // reference is always a past running maximum, so some key of the row has
 // P >= 1 and nothing underflows that the exact recurrence keeps; P <= 2^8
 // and l <= Sk 2^8 stay far inside fp32 and bf16 range, and rounding is
@@ -326,11 +327,13 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
     //  - D = 128: in the matrix phase, one v_mfma_f32_16x16x32_bf16 per
     //    16-key chunk accumulated into lacc across tiles, with P stored in
     //    place in the score accumulators (kPInPlace);
-    //  - D = 64: in the softmax phase, the four chunks' MFMAs into a fresh
-    //    accumulator right after the exponentials.  That tile sum is the
-    //    check of the lagged reference (below) and is then added to l.  P
-    //    goes to separate registers, since the check may need the scores
-    //    again after P is taken.
+    //  - D = 64: at the start of the matrix phase, the four chunks' MFMAs
+    //    into a fresh accumulator.  That tile sum is the check of the
+    //    lagged reference (below) and is then added to l.  P goes to
+    //    separate registers, since the check may need the scores again
+    //    after P is taken.  (Taken at the end of the softmax phase instead,
+    //    these MFMAs wait there for a matrix core that the other group
+    //    keeps busy, and that phase ends the slot.)
     // (A vector sum, v_dot2c_f32_bf16 of each rounded pair with (1, 1), waits
     // for a busy matrix core and issues 16 more vector instructions per
     // tile.)
@@ -469,46 +472,48 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
 #pragma unroll
             for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
         } else {
-            // fast path: P against the row's current reference, without the
-            // tile maximum.  It stands when the row's sum of P for the tile
-            // is at most 2^kLag (so no single P exceeds it) and the row has a
-            // reference.
-            {
-                const float mu = guard_max(m);
+            // P against the row's current reference, without the tile
+            // maximum; the matrix phase checks it (check below)
+            const float mu = guard_max(m);
 #pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
-            }
-            float rs = tile_sum();
-            const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
-            if (__builtin_amdgcn_ballot_w64(redo)) {
-                // slow path (the first tile of a row, a large rise, or a
-                // NaN): the reference moves to the running maximum, O and l
-                // follow it, and P is taken again against it
-                float mx = kNegInf;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-                mx = fmaxf(mx, xor32(mx));
-                const float ms = mx * c;
-                const bool up = ms > m;                   // m = -inf: any finite score moves it
-                const float mn = up ? ms : m;
-                const float mu = guard_max(mn);
-                const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
-#pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
-                rs = tile_sum();
-                l *= alpha;
-                m = mn;
-                if (__builtin_amdgcn_ballot_w64(up)) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                }
-            }
-            l += rs;
+            for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
         }
+    };
+    // D = 64, at the start of the matrix phase M(t), before P(t) meets V:
+    // the P of the softmax phase stands when the row's sum of it for the
+    // tile is at most 2^kLag (so no single P exceeds it) and the row has a
+    // reference
+    auto check = [&]() __attribute__((always_inline)) {
+        float rs = tile_sum();
+        const bool redo = m == kNegInf || !(rs <= kMaxTileSum);
+        if (__builtin_amdgcn_ballot_w64(redo)) {
+            // slow path (the first tile of a row, a large rise, or a
+            // NaN): the reference moves to the running maximum, O and l
+            // follow it, and P is taken again against it
+            float mx = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mx = fmaxf(mx, xor32(mx));
+            const float ms = mx * c;
+            const bool up = ms > m;                   // m = -inf: any finite score moves it
+            const float mn = up ? ms : m;
+            const float mu = guard_max(mn);
+            const float alpha = exp2_hw(m - mu);      // exactly 1 where the reference stays
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) exp_pair(pp, mu);
+            rs = tile_sum();
+            l *= alpha;
+            m = mn;
+            if (__builtin_amdgcn_ballot_w64(up)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+        }
+        l += rs;
     };
 
     // ---- prologue: K(0), V(0), K(1) into LDS; each wave's rows of Q, loaded
@@ -556,6 +561,7 @@ __global__ __launch_bounds__(64 * NW, NW / 4) void attn_fwd_kernel(const uint16_
         if (grp == 0) loads(t, par);
         if (t <= tlast) {
             __builtin_amdgcn_s_setprio(1);  // this wave's MFMAs go ahead of its partner's vector work
+            if constexpr (!kPInPlace) check();
             mphase(std::true_type{}, std::true_type{}, reinterpret_cast<const char*>(sV[P]),
                    reinterpret_cast<const char*>(sK[P ^ 1]));
             __builtin_amdgcn_s_setprio(0);
