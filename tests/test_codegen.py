@@ -69,5 +69,5 @@ def test_attention_row_sum_on_matrix_core(kernels):
         assert "v_dot2" not in code, f"{name}: vector dot2 in the attention kernel"
         sel = len(re.findall(r"v_mfma_f32_16x16x32_bf16", code))
         # four 16-key chunks per 64-key tile, the loop unrolled two tiles deep;
-        # at D = 64 the softmax phase's fast and slow paths each take the sum
+        # at D = 64 the lag check and its second pass each take the sum
         assert sel in (8, 16), f"{name}: {sel} selector MFMAs"
